@@ -1,0 +1,214 @@
+"""Benchmark of the MXFP4 MoE expert layer on one MI355X.
+
+A step is one layer call (router, top-k, permutation, MXFP4 gate/up + SwiGLU,
+MXFP4 down, combine) over one synthetic batch, through the C ABI's single
+persistent launch.  Default workload: the speculative-verify block (T=8
+tokens, d=7168, ffn=2048, 256 experts, top-8).  Inputs are resident in HBM
+before timing; the expert weights are rotated over `--replicas` distinct
+copies (distinct layers) so that consecutive steps never re-read bytes that
+could still sit in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth
+(bytes the layer must move / time per layer): every active expert's packed
+codes and scales once, the router weights, x and the fp32 output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/layer + achieved HBM GB/s (% of peak), MXFP4 MoE, 8-token verify block"
+HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10100.0
+KERNEL_SOURCES = ["mxfp4_moe_expert_router_amd/csrc/moe_layer.hip", "mxfp4_moe_expert_router_amd/csrc/moe_device.h"]
+
+
+def kernel_hash() -> str:
+    m = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            m.update(f.read())
+    return m.hexdigest()[:16]
+
+
+def traffic_record(workload: str):
+    """HBM traffic per launch measured with rocprofv3 counters (profiles/), if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="verify",
+                    choices=["tiny", "decode", "verify", "batched_verify", "dense"])
+    ap.add_argument("--replicas", type=int, default=4, help="distinct copies of the expert weights")
+    ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding (expert or tensor parallel) "
+                                   "is described in the design notes but not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_router_amd as moe
+    from synth import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.get_config(args.workload)
+    t_gen = time.time()
+    x, wr = synth.routing_inputs(cfg)
+    p, s = synth.expert_weights(cfg)
+    gen_s = time.time() - t_gen
+    print(f"[bench] inputs generated in {gen_s:.1f} s (workload {args.workload})", file=sys.stderr, flush=True)
+
+    xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    wrt = torch.from_numpy(wr).to(dev)
+    pt0 = torch.from_numpy(p).to(dev)
+    st0 = torch.from_numpy(s).to(dev)
+    reps_p, reps_s = [pt0], [st0]
+    for _ in range(max(1, args.replicas) - 1):
+        reps_p.append(pt0.clone())
+        reps_s.append(st0.clone())
+    R = len(reps_p)
+    dims = moe.LayerDims(cfg.T, cfg.d, cfg.F, cfg.E)
+    ws = moe.alloc_workspace(dims, cfg.k, dev)
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    wsb = ws.numel()
+
+    def step(i):
+        st = moe.forward_raw(dims, xt.data_ptr(), wrt.data_ptr(), reps_p[i % R].data_ptr(),
+                             reps_s[i % R].data_ptr(), cfg.k, out.data_ptr(), ws.data_ptr(), wsb, sh,
+                             staged=args.staged)
+        if st != 0:
+            raise moe.MoeError(st, "forward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if moe.status(ws) != moe.MOE_OK:
+        raise RuntimeError("device watchdog fired during warmup")
+
+    # timed region: K steps, per-launch HIP events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if moe.status(ws) != moe.MOE_OK:
+        raise RuntimeError("device watchdog fired during the timed steps")
+    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+    it = moe.intermediates(ws, dims, cfg.k)
+    n_active = int(it["n_active"].item())
+    alg_bytes = synth.algorithmic_bytes(cfg, n_active)
+    flops = synth.layer_flops(cfg)
+    ms_per_step = elapsed * 1e3 / args.steps
+    us_layer = ms_per_step * 1e3
+    gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_ms = float(launch_ms.mean())
+    kern_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    traffic = None
+    trec = traffic_record(args.workload + ("_staged" if args.staged else ""))
+    if trec is not None:
+        traffic = trec.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "dtype_detail": "MXFP4 (E2M1 + E8M0) weights, bf16 activations, bf16x2 dot / fp32 FMA, fp32 accumulation",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: T={cfg.T} d={cfg.d} ffn={cfg.F} E={cfg.E} top-{cfg.k}"
+                        + (f" Zipf(s={cfg.zipf_s})" if cfg.zipf_s else ""),
+            "T": cfg.T, "d": cfg.d, "ffn": cfg.F, "E": cfg.E, "topk": cfg.k,
+            "route_seed": cfg.route_seed, "active_experts": n_active,
+            "weight_replicas": R, "path": "staged (one launch per step)" if args.staged else "persistent single launch",
+        },
+        "us_per_layer": round(us_layer, 2),
+        "tokens_per_s_per_layer": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes": alg_bytes,
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "k_persistent" if not args.staged else "k_gate_up+k_down (staged)",
+            "kernel_us_mean": round(kern_ms * 1e3, 2),
+            "kernel_us_p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
+            "kernel_us_p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2),
+            "mfma_frac_of_mxfp4_peak_if_all_flops_on_mfma": round(flops / (kern_ms * 1e-3) / 1e12
+                                                                   / MXFP4_PEAK_TFLOPS, 5),
+        },
+        "kernel_hash": kernel_hash(),
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        nth = args.cpu_threads or min(16, os.cpu_count() or 1)
+        mask = None
+        sample = f"the whole {args.workload} layer (all {cfg.T} tokens)"
+        if cfg.T > 8:  # bound the CPU work: a sample of tokens, scaled per token
+            mask = np.zeros(cfg.T, dtype=np.uint8)
+            mask[:: max(1, cfg.T // 8)] = 1
+            sample = f"{int(mask.sum())} of {cfg.T} tokens of the {args.workload} layer (all routing)"
+        t1 = time.perf_counter()
+        oracle.forward(x, wr, p, s, cfg.k, cfg.F, token_mask=mask, nthreads=nth)
+        cpu_s = time.perf_counter() - t1
+        frac = 1.0 if mask is None else float(mask.sum()) / cfg.T
+        cpu_layer_s = cpu_s / frac
+        result["cpu_baseline"] = {
+            "value": round(alg_bytes / cpu_layer_s / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nth,
+            "kind": "oracle",
+            "sample": sample + f"; fp64 C oracle, {cpu_s:.2f} s wall, {nth} OpenMP threads",
+            "us_per_layer": round(cpu_layer_s * 1e6, 1),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

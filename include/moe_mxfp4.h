@@ -1,0 +1,205 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MXFP4 MoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * One call runs one Mixture-of-Experts layer over a block of T tokens:
+ *   router logits -> top-k experts and gates -> token-to-expert permutation
+ *   -> MXFP4-dequant gate/up projections with SwiGLU -> MXFP4 down projection
+ *   -> gate-weighted combine.
+ * All of it runs in HIP kernels on the GPU; the host side only validates
+ * arguments and enqueues work on the caller's stream.
+ *
+ * Sources (pages on the MiMo x TileRT system; cited by title and section):
+ *  [P1-FP4]  "MiMo x TileRT" article (blog.hypho.cn), section "第一层：FP4 选择性量化":
+ *            MoE expert weights are OCP MXFP4, the router keeps a higher precision.
+ *  [P1-BG]   same article, section "万亿参数推理为什么特别难": each token activates a
+ *            few experts and decode speed is bounded by bandwidth / bytes per token.
+ *  [P3-FP4]  "MiMo 把 1T 模型推到每秒千 token——FP4、DFlash 與常駐 kernel 的三層
+ *            co-design" (vatt-ghern.pages.dev), section "FP4：只量化 MoE expert，其餘
+ *            維持原精度": small blocks of 4-bit values share one scale; top-k routing
+ *            is precision sensitive.
+ *  [P3-PK]   same page, section "persistent engine kernel 與 warp specialization":
+ *            one resident kernel instead of one launch per operator.
+ *  [P3-DF]   same page, section "DFlash：block-level masked 並行草稿": one target
+ *            forward verifies a block of 8 drafted positions.
+ *  [P5-FP4]  "tech-implementation-2026-06-09" (shengyayun.com), section "关键实现细节
+ *            / 1.": the quantized linears are the experts' gate_proj, up_proj, down_proj.
+ *  [P5-TRT]  same page, section "3. TileRT 的"持久化内核"到底做了什么": per layer, the
+ *            MoE gate then the expert compute; per-op launches leave gaps.
+ *  [MX]      OCP Microscaling Formats v1.0 (listed among the pages' sources): E2M1
+ *            elements, 32-element blocks, E8M0 scales 2^(s-127).
+ *
+ * Data layout (all row-major; K is the contiguous, reduced dimension):
+ *  x              bf16 [T][d]                               (device)
+ *  router_w       fp32 [E][d]                               (device)
+ *  packed_experts uint8, expert e at byte e*moe_mxfp4_expert_packed_bytes(d, F):
+ *                   gate [F][d/2] | up [F][d/2] | down [d][F/2]
+ *                 element c of a row is in byte c/2 of that row, low nibble for
+ *                 even c, high nibble for odd c; each nibble is an E2M1 code.
+ *  scales         uint8, expert e at byte e*moe_mxfp4_expert_scale_bytes(d, F):
+ *                   gate [F][d/32] | up [F][d/32] | down [d][F/32]
+ *                 one E8M0 byte per 32 consecutive elements of a row.
+ *  out            fp32 [T][d]                               (device, overwritten)
+ *
+ * Semantics (readings where the pages are silent):
+ *  logit[t][e] = sum_c x[t][c] * router_w[e][c], fp32 accumulation;
+ *  top-k: the k largest logits of a token, ties toward the lower expert index;
+ *  gate[t][j] = softmax over the k selected logits;
+ *  h = silu(W_gate x_t) * (W_up x_t), y = W_down h (dequantized weights, fp32
+ *  accumulation, h kept in fp32);
+ *  out[t] = sum_j gate[t][j] * y(expert_j, t), summed in top-k order.
+ *  Supported scale bytes on the GPU: 1..254 (0 decodes as 0, 255 as +inf).
+ *
+ * Ownership and concurrency: the caller allocates and frees every buffer.  The
+ * library never allocates device memory, never synchronizes (except
+ * moe_mxfp4_status) and returns as soon as the work is enqueued on `stream`
+ * (a hipStream_t; NULL is the default stream).  Inputs are read-only.  A
+ * workspace must not be shared by two calls that may run concurrently; its
+ * contents other than the synchronization header are undefined after a call.
+ *
+ * Errors: every entry point returns a moe_status.  Host-side validation
+ * happens before anything is enqueued; on an error nothing runs.  With T = 0
+ * (valid sizes) a call does nothing and returns MOE_OK without looking at the
+ * buffer pointers.  Device faults surface at the caller's next
+ * synchronization, as for any HIP call.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,     /* null pointer, topk outside [1, E], negative T, bad option   */
+  MOE_ESHAPE = 2,     /* d or ffn not a multiple of 32, or a size above the limits   */
+  MOE_EWORKSPACE = 3, /* workspace smaller than moe_mxfp4_workspace_bytes()          */
+  MOE_ELAUNCH = 4,    /* the HIP launch failed                                       */
+  MOE_ETIMEOUT = 5,   /* a device-side wait exceeded its limit; the kernel exited    */
+  MOE_EDEVICE = 6,    /* HIP device query / copy failed                              */
+  MOE_EALIGN = 7      /* x, router_w, packed_experts or out not 16-byte aligned,
+                         workspace not 256-byte aligned                              */
+} moe_status;
+
+/* Layer sizes: T tokens, hidden size d, expert ffn size, E experts.  Limits:
+ * T >= 0, d and ffn multiples of 32, 32 <= d <= 16384, 32 <= ffn <= 8192, 1 <= E <= 1024,
+ * E * ceil(T / 64) <= 4096 (so T <= 1024 with 256 experts), 1 <= topk <= min(E, 64). */
+typedef struct {
+  int32_t T;
+  int32_t d;
+  int32_t ffn;
+  int32_t E;
+} moe_mxfp4_dims;
+
+/* Bytes of one expert's packed codes: 3*d*ffn/2 ([P5-FP4] three linears per expert). */
+size_t moe_mxfp4_expert_packed_bytes(int32_t d, int32_t ffn);
+
+/* Bytes of one expert's E8M0 scales: 3*d*ffn/32 ([P3-FP4] one scale per block). */
+size_t moe_mxfp4_expert_scale_bytes(int32_t d, int32_t ffn);
+
+/* Size of the device workspace moe_mxfp4_forward needs for these sizes (0 on
+ * invalid sizes).  It holds a synchronization header, the router's partial
+ * logits, the top-k results, the SwiGLU activations h [T*topk][ffn] and the
+ * gated expert outputs [T*topk][d] as epoch-tagged 64-bit words, and plain
+ * copies of the routing results for inspection. */
+size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_dims* dims, int32_t topk);
+
+/* Zero a whole workspace on `stream` (a fill kernel, safe under stream
+ * capture).  A workspace must be zero-filled before its first forward call
+ * (allocating it zeroed is enough); afterwards every call leaves it valid for
+ * the next one.  Call it again after a forward call that timed out. */
+int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer in ONE persistent kernel launch ([P3-PK], [P5-TRT]): router,
+ * top-k, permutation, expert gate/up+SwiGLU, down projection and combine.
+ * The grid is one workgroup per CU, all co-resident (cooperative launch); the
+ * steps hand data to each other through epoch-tagged words that consumers
+ * poll, so no host round trip, grid barrier or device-wide atomic separates
+ * them.  The MoE gate is [P1-FP4]/[P3-FP4]'s higher-precision router; the
+ * experts are [P5-FP4]'s MXFP4 gate/up/down.
+ *   dims            sizes (host pointer)
+ *   x               bf16 [T][d] device, 16-byte aligned
+ *   router_w        fp32 [E][d] device, 16-byte aligned
+ *   packed_experts  E2M1 codes, layout above, device, 16-byte aligned
+ *   scales          E8M0 bytes, layout above, device
+ *   topk            experts per token, 1 <= topk <= min(E, 64)
+ *   out             fp32 [T][d] device, 16-byte aligned, fully overwritten
+ *   workspace       device, 256-byte aligned, >= moe_mxfp4_workspace_bytes(),
+ *                   zero-filled before its first use
+ *   stream          hipStream_t
+ * Returns MOE_OK once enqueued.  Every device-side wait has a watchdog (2 s);
+ * a wait that does not finish makes the kernel exit early and sets the status
+ * word that moe_mxfp4_status() returns as MOE_ETIMEOUT. */
+int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                      const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same layer and the same result bit for bit, as one kernel launch per step
+ * ([P5-TRT]'s per-operator model), for measuring what the single launch saves. */
+int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                             const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of moe_mxfp4_forward_ex. */
+typedef struct {
+  uint32_t flags;         /* MOE_OPT_* bits                                           */
+  uint32_t spin_limit_us; /* device wait limit in microseconds; 0 = default (2 s)      */
+  int32_t grid;           /* workgroups of the persistent launch; 0 = all co-resident  */
+} moe_mxfp4_options;
+
+/* Test knob: the top-k step waits for router results tagged for a call that
+ * never happens, so every workgroup reaches its watchdog and the kernel exits
+ * with MOE_ETIMEOUT. */
+#define MOE_OPT_WITHHOLD_ARRIVAL 0x1u
+
+/* moe_mxfp4_forward with options (opts may be NULL). */
+int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                         const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
+                         float* out, void* workspace, size_t workspace_bytes,
+                         const moe_mxfp4_options* opts, void* stream);
+
+/* Routing only ([P1-BG] each token to a few experts; [P3-FP4] top-k): runs the
+ * router, top-k and permutation kernels of the layer and copies their results
+ * (device buffers):
+ *   topk_idx       int32 [T][topk]  experts of each token, (logit desc, index asc)
+ *   topk_w         fp32  [T][topk]  gates
+ *   expert_offsets int32 [E+1]      pairs routed to experts < e
+ *   sorted_slot    int32 [T*topk]   pair p's slot t*topk + j; pairs ordered by
+ *                                   (expert asc, token asc)
+ * Any output pointer may be NULL.  Same validation as moe_mxfp4_forward. */
+int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* router_w, int32_t topk,
+                    int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* sorted_slot,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Byte offsets of the intermediates inside a workspace after a forward call
+ * (for inspection).  h = SwiGLU activations [T*topk][ffn] in pair order (the
+ * order of sorted_slot) and y = gated expert outputs [T*topk][d] in slot order
+ * (row t*topk + j holds gate[t][j] * y(expert_j, t)) are 64-bit words whose low
+ * 32 bits are the fp32 value (the high 32 bits are a tag); logits fp32 [T][E];
+ * topk_idx int32 [T][topk]; topk_w fp32 [T][topk]; offsets int32 [E+1];
+ * sorted_slot, pos int32 [T*topk]; active int32 [E] (experts with at least one
+ * token, ascending); n_active int32. */
+typedef struct {
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, total;
+} moe_mxfp4_ws_layout;
+int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxfp4_ws_layout* layout);
+
+/* Wait for `stream`, then read and clear the workspace's device status word:
+ * MOE_OK, or MOE_ETIMEOUT if a device wait of the last call(s) timed out. */
+int moe_mxfp4_status(void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* moe_mxfp4_strerror(int status);
+
+/* Grid (workgroups) the persistent launch uses on the current device for these
+ * sizes, or a negative moe_status. */
+int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

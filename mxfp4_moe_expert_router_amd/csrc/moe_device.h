@@ -1,0 +1,202 @@
+// Device-side building blocks for the MXFP4 MoE layer on gfx950 (CDNA4, wave64).
+//
+// MXFP4 ([MX]: OCP Microscaling v1.0, the format the "MiMo x TileRT" pages name
+// for the experts): E2M1 codes, two per byte (even element in the low nibble),
+// one E8M0 scale byte per 32 elements.  Decoding uses gfx950's scaled FP4
+// converts, which turn one byte (two codes) into two bf16 or two fp32 values
+// multiplied by the block scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// E8M0 byte s -> 2^(s-127) as fp32, by placing s in the exponent field.
+// Exact for s in [1, 254]; s = 0 gives 0 and s = 255 gives +inf.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __builtin_bit_cast(float, s << 23);
+}
+
+// Byte `sel` (0..3) of `w` -> two bf16 (low nibble in .x), times `scale`.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL);
+}
+
+// Byte `sel` (0..3) of `w` -> two fp32 (low nibble in .x), times `scale`.
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+// acc + a.x*b.x + a.y*b.y (bf16 products, fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// 32 packed codes (one 16-byte load, one block) against 32 bf16 activations
+// held as four 16-byte pieces (piece q = elements 8q..8q+7).
+__device__ __forceinline__ float dot32_bf16(const u32x4_t w, float scale, const u32x4_t* xq, float acc) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t xv = xq[q];
+    acc = dot2_bf16(fp4x2_to_bf16x2<0>(ws[q], scale), xv.x, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<1>(ws[q], scale), xv.y, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<2>(ws[q], scale), xv.z, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<3>(ws[q], scale), xv.w, acc);
+  }
+  return acc;
+}
+
+// 32 packed codes (one 16-byte chunk) -> 32 fp32 values times the block scale.
+__device__ __forceinline__ void decode32_f32(const u32x4_t w, float scale, float (&v)[32]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x2_t a;
+    a = fp4x2_to_f32x2<0>(ws[q], scale);
+    v[8 * q + 0] = a.x;
+    v[8 * q + 1] = a.y;
+    a = fp4x2_to_f32x2<1>(ws[q], scale);
+    v[8 * q + 2] = a.x;
+    v[8 * q + 3] = a.y;
+    a = fp4x2_to_f32x2<2>(ws[q], scale);
+    v[8 * q + 4] = a.x;
+    v[8 * q + 5] = a.y;
+    a = fp4x2_to_f32x2<3>(ws[q], scale);
+    v[8 * q + 6] = a.x;
+    v[8 * q + 7] = a.y;
+  }
+}
+
+// acc + sum_i v[i] * h[i] over 32 values, fp32 FMA in index order.
+__device__ __forceinline__ float dot32(const float (&v)[32], const float* h, float acc) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc = fmaf(v[i], h[i], acc);
+  return acc;
+}
+
+// 16-byte streaming load of weight bytes that are read exactly once per call.
+__device__ __forceinline__ u32x4_t ld_stream16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// Value known to be equal in all lanes of the wave, moved to a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// bf16 bits -> fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+// Row-level steps use DPP (xor 1, xor 2, half-row mirror, row mirror), the
+// cross-row steps use bpermute shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Eight per-lane partial sums v[0..7] -> every lane receives the wave-wide
+// total of value (lane >> 3).  Reduce-scatter: exchange half of the values
+// across lane bits 5, 4 and 3, then sum the remaining value over lane bits
+// 0..2.  Costs ~30 VALU ops and 6 shuffles instead of 8 full reductions.
+__device__ __forceinline__ float reduce8(const float v[8]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  float w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b5 ? v[i + 4] : v[i];
+    const float send = b5 ? v[i] : v[i + 4];
+    w[i] = keep + __shfl_xor(send, 32, kWave);
+  }
+  float x[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b4 ? w[i + 2] : w[i];
+    const float send = b4 ? w[i] : w[i + 2];
+    x[i] = keep + __shfl_xor(send, 16, kWave);
+  }
+  float y;
+  {
+    const float keep = b3 ? x[1] : x[0];
+    const float send = b3 ? x[0] : x[1];
+    y = keep + dpp_f<0x128>(send);  // row_ror:8 = lane ^ 8 within a row of 16
+  }
+  y += dpp_f<0xB1>(y);   // xor 1
+  y += dpp_f<0x4E>(y);   // xor 2
+  y += dpp_f<0x141>(y);  // half-row mirror: the other quad of the 8
+  return y;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- atomics ---
+__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_release(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Epoch-tagged 32-bit values: {value, tag} in one 64-bit word, written and
+// read with single-copy-atomic agent-scope accesses (coherent across the
+// chip's L2 slices without cache flushes).  A consumer accepts a word only if
+// its tag equals the current call's tag, so no barrier or fence is needed
+// between producer and consumer, and stale words of earlier calls never pass.
+__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t bits, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ float tag_f32(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
+__device__ __forceinline__ int tag_i32(uint64_t w) { return (int)(uint32_t)w; }
+
+}  // namespace moe

@@ -1,0 +1,1309 @@
+// MXFP4 MoE expert layer for AMD Instinct MI355X (gfx950): kernels and C ABI.
+//
+// The layer (router -> top-k -> permutation -> MXFP4 gate/up + SwiGLU -> MXFP4
+// down -> gate-weighted combine) follows the pages on the MiMo x TileRT system:
+//  [P1-FP4] "MiMo x TileRT" (blog.hypho.cn), section "第一层：FP4 选择性量化":
+//           experts in OCP MXFP4, router at higher precision;
+//  [P1-BG]  same article, section "万亿参数推理为什么特别难": a token activates a
+//           few experts; decode is bounded by bytes read per token;
+//  [P3-FP4] "MiMo 把 1T 模型推到每秒千 token——FP4、DFlash 與常駐 kernel 的三層
+//           co-design" (vatt-ghern.pages.dev), section "FP4：只量化 MoE expert，
+//           其餘維持原精度": 4-bit blocks sharing one scale; precision-sensitive top-k;
+//  [P3-PK]  same page, section "persistent engine kernel 與 warp specialization":
+//           the pipeline as one resident kernel, no launch per operator;
+//  [P5-FP4] "tech-implementation-2026-06-09" (shengyayun.com), section "关键实现细节
+//           / 1.": expert gate_proj / up_proj / down_proj are the MXFP4 linears;
+//  [P5-TRT] same page, section "3. TileRT 的"持久化内核"到底做了什么": MoE gate then
+//           expert compute inside one resident kernel.
+//
+// Execution model.  The whole layer is ONE cooperative launch whose grid is
+// one 512-thread workgroup per CU (all co-resident).  Steps hand data to each
+// other through epoch-tagged words: a 64-bit {value, tag} written and read
+// with single-copy-atomic, agent-coherent accesses.  A consumer spins (with a
+// wall-clock watchdog) until the words it needs carry the current call's tag.
+// There are no grid barriers, no cache-flushing fences and no read-modify-
+// write atomics on the path: on MI355X one grid barrier over 256 workgroups
+// costs tens of microseconds because device-scope atomics to one address
+// serialize, while a tagged word costs one coherent store.  Deadlock freedom:
+// every workgroup runs the steps in the same order and a step only waits on
+// words produced by earlier steps of (possibly other) co-resident workgroups.
+//
+// Steps:
+//   router   units (expert, half of d, 8 tokens), one wave each -> tagged partial logits
+//   top-k    small batches: every workgroup redundantly, from the tagged logits;
+//            large batches: one wave per token -> tagged expert ids and gates
+//   permute  every workgroup builds the (expert, token) permutation in LDS
+//   gate/up  small batches: all of x resident in LDS, each wave streams a
+//            contiguous range of (expert, row) pairs of W_gate/W_up;
+//            large batches: workgroup units with x staged per token group
+//            -> tagged h = silu(W_gate x) * (W_up x)
+//   down     each wave streams a contiguous range of (expert, row) of W_down,
+//            8 rows per step, h of the expert's tokens held in registers
+//            -> tagged gate * y in the token's slot
+//   combine  out[t] = sum of the token's k slots, in slot order
+//
+// Hot loops: a lane owns 16-byte chunks (32 codes = one scale block) of a row,
+// so a wave-wide load reads 1 KiB contiguous; the next rows' loads are issued
+// before the current rows are computed.  gate/up decode codes to bf16 with the
+// block scale folded in (v_cvt_scalef32_pk_bf16_fp4) and use bf16 dot2 with
+// fp32 accumulation (x is bf16 and every E2M1 * 2^k is exact in bf16); down
+// decodes to fp32 (v_cvt_scalef32_pk_f32_fp4) and uses fp32 FMA so h is never
+// rounded.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "moe_device.h"
+#include "moe_mxfp4.h"
+
+namespace moe {
+
+constexpr int kWG = 512;               // threads per workgroup
+constexpr int kWaves = kWG / kWave;    // waves per workgroup
+constexpr int kLdsMax = 160 * 1024 - 1024;  // dynamic LDS per workgroup (gfx950 has 160 KiB; static LDS needs a few bytes)
+constexpr int kRouterParts = 2;        // a router unit covers d / kRouterParts columns
+constexpr int kRouterTok = 8;          // tokens per router unit
+constexpr int kRouterF4 = 16;          // float4 per lane per router unit (d <= 8192)
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kMaxD = 8192;
+constexpr int kMaxF = 4096;
+constexpr int kGUChunks = 4;           // 16-byte chunks per lane of a d-row (d <= 8192)
+constexpr int kRowsGU = 16;            // rows per workgroup unit (large batches)
+constexpr int kMaxTokLds = 8;          // token rows per x staging pass (large batches)
+constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
+constexpr int kMaxGrid = 2048;
+constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
+
+// Header words (first kHdrBytes of the workspace).
+enum { kEpoch = 0, kStatus = 1, kAbort = 2, kStarted = 64 };
+constexpr size_t kHdrBytes = (size_t)(kStarted + kMaxGrid) * 4;
+
+struct Params {
+  int T, d, F, E, k;
+  const uint16_t* x;
+  const float* wr;
+  const uint8_t* packed;
+  const uint8_t* scales;
+  float* out;
+  uint32_t* hdr;
+  uint64_t* lgp;   // [T][E][kRouterParts] tagged partial logits
+  uint64_t* tki;   // [T*k] tagged expert ids   (large batches)
+  uint64_t* tkw;   // [T*k] tagged gates        (large batches)
+  uint64_t* hq;    // [T*k][F] tagged h, pair order
+  uint64_t* yq;    // [T*k][d] tagged gate * y, slot order
+  float* logits;   // plain copies for inspection
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* offsets;
+  int32_t* sorted_slot;
+  int32_t* pos;
+  int32_t* active;
+  int32_t* n_active;
+  uint64_t spin_ticks;
+  uint32_t withhold;  // test knob: top-k waits for a tag the router never writes
+  int ntl;            // tokens per x staging pass (large batches)
+};
+
+// ------------------------------------------------------------ LDS layout ----
+// Shared by host (size) and device (carving).
+struct LdsPlan {
+  size_t xs, mask, tki, tkw, off, slot, act, misc, total;
+};
+
+__host__ __device__ inline size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+__host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool small, int ntl) {
+  LdsPlan L;
+  const size_t TK = (size_t)T * k;
+  const size_t W = ((size_t)T + 63) / 64;
+  const size_t mask_bytes = (size_t)E * W * 8;
+  size_t o = 0;
+  if (small) {
+    // x of all tokens stays resident; the permutation masks get their own space
+    L.xs = o; o = al16(o + (size_t)T * d * 2);
+    L.mask = o; o = al16(o + mask_bytes);
+  } else {
+    // x is staged after the permutation is built: the masks alias the x region
+    size_t xs_bytes = (size_t)ntl * d * 2;
+    if (mask_bytes > xs_bytes) xs_bytes = mask_bytes;
+    L.xs = o; L.mask = o; o = al16(o + xs_bytes);
+  }
+  L.tki = o; o = al16(o + TK * 4);
+  L.tkw = o; o = al16(o + TK * 4);
+  L.off = o; o = al16(o + ((size_t)E + 1) * 4);
+  L.slot = o; o = al16(o + TK * 4);
+  L.act = o; o = al16(o + (size_t)E * 4);
+  L.misc = o; o = al16(o + 64 * 4);
+  L.total = o;
+  return L;
+}
+
+struct Smem {
+  u32x4_t* xs;
+  uint64_t* mask;
+  int* tki;
+  float* tkw;
+  int* off;
+  int* slot;
+  int* act;
+  int* misc;  // [0] n_active, [8..8+kWaves) scan scratch
+};
+
+// `ntl`: x staging rows of the kernel's layout (0 if it stages no x).
+__device__ __forceinline__ Smem carve(char* base, const Params& P, bool small, int ntl) {
+  const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small, ntl);
+  Smem S;
+  S.xs = reinterpret_cast<u32x4_t*>(base + L.xs);
+  S.mask = reinterpret_cast<uint64_t*>(base + L.mask);
+  S.tki = reinterpret_cast<int*>(base + L.tki);
+  S.tkw = reinterpret_cast<float*>(base + L.tkw);
+  S.off = reinterpret_cast<int*>(base + L.off);
+  S.slot = reinterpret_cast<int*>(base + L.slot);
+  S.act = reinterpret_cast<int*>(base + L.act);
+  S.misc = reinterpret_cast<int*>(base + L.misc);
+  return S;
+}
+
+// ------------------------------------------------------------ watchdog ------
+
+__device__ __forceinline__ bool aborted(const Params& P, uint32_t tag) {
+  return ld_relaxed(&P.hdr[kAbort]) == tag;
+}
+
+__device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag) {
+  st_relaxed(&P.hdr[kStatus], (uint32_t)MOE_ETIMEOUT);
+  st_relaxed(&P.hdr[kAbort], tag);
+}
+
+// One spin round of a wave-level wait: true to retry, false to give up.
+__device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint64_t t0) {
+  if (aborted(P, tag)) return false;
+  if (wall_clock64() - t0 > P.spin_ticks) {
+    raise_timeout(P, tag);
+    return false;
+  }
+  __builtin_amdgcn_s_sleep(2);
+  return true;
+}
+
+// Tag of this call: epoch + 1, never 0 (a zero-filled workspace has tag 0).
+__device__ __forceinline__ uint32_t start_call(const Params& P, int wg, bool mark_started) {
+  __shared__ uint32_t s_tag;
+  if (threadIdx.x == 0) {
+    const uint32_t e = ld_relaxed(&P.hdr[kEpoch]);
+    s_tag = e + 1u;
+    if (mark_started) st_relaxed(&P.hdr[kStarted + wg], e + 1u);
+  }
+  __syncthreads();
+  return s_tag;
+}
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t tag) { return tag >= 0xFFFFFFFEu ? 0u : tag; }
+
+// Workgroup 0 closes the call: once every workgroup has read the epoch, the
+// epoch advances so that the next call's tag differs from every word written
+// by this one.
+__device__ __forceinline__ void end_call(const Params& P, uint32_t tag, int G) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      bool ok = true;
+      for (int w = lane; w < G; w += kWave) ok &= (ld_relaxed(&P.hdr[kStarted + w]) == tag);
+      if (__all(ok)) break;
+      if (wall_clock64() - t0 > P.spin_ticks) {
+        if (lane == 0) raise_timeout(P, tag);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) st_relaxed(&P.hdr[kEpoch], next_epoch(tag));
+  }
+}
+
+// ---------------------------------------------------------------- router ----
+// logits[t][e] = sum_c x[t][c] * W_r[e][c] in fp32 ([P1-FP4]/[P3-FP4]: the
+// router stays at higher precision than the experts).  Unit = (expert, part
+// of d, group of 8 tokens), one wave; the two partial sums of a logit are
+// added in a fixed order by the consumer.
+__device__ __forceinline__ void router_step(const Params& P, uint32_t tag, int gw, int NW) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ngr = (P.T + kRouterTok - 1) / kRouterTok;
+  const int nunits = P.E * kRouterParts * ngr;
+  const int dp = P.d / kRouterParts;
+  const int n4 = dp / 4;
+  for (int u = gw; u < nunits; u += NW) {
+    const int g = u % ngr;
+    const int part = (u / ngr) % kRouterParts;
+    const int e = u / (ngr * kRouterParts);
+    const int t0 = g * kRouterTok, nt = min(kRouterTok, P.T - t0);
+    const int c0 = part * dp;
+    const float4* w = reinterpret_cast<const float4*>(P.wr + (size_t)e * P.d + c0);
+    float4 wv[kRouterF4];
+#pragma unroll
+    for (int i = 0; i < kRouterF4; ++i) {
+      const int c = lane + kWave * i;
+      wv[i] = (c < n4) ? w[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float acc[kRouterTok];
+#pragma unroll
+    for (int j = 0; j < kRouterTok; ++j) {
+      acc[j] = 0.f;
+      if (j < nt) {
+        const uint16_t* xt = P.x + (size_t)(t0 + j) * P.d + c0;
+#pragma unroll
+        for (int i = 0; i < kRouterF4; ++i) {
+          const int c = lane + kWave * i;
+          if (c < n4) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(xt + (size_t)c * 4);
+            acc[j] = fmaf(wv[i].x, bf16lo(xv.x), acc[j]);
+            acc[j] = fmaf(wv[i].y, bf16hi(xv.x), acc[j]);
+            acc[j] = fmaf(wv[i].z, bf16lo(xv.y), acc[j]);
+            acc[j] = fmaf(wv[i].w, bf16hi(xv.y), acc[j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRouterTok; ++j) {
+      const float s = wave_sum(acc[j]);
+      if (lane == j && j < nt)
+        st_tagged(&P.lgp[((size_t)(t0 + j) * P.E + e) * kRouterParts + part], __builtin_bit_cast(uint32_t, s), tag);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k -----
+// One wave, token t: gathers the tagged logits, selects the k largest in
+// (logit desc, expert asc) order and their softmax over the selected set
+// ([P3-FP4] top-k routing).  Lane j < k returns expert j and gate j.
+// Returns false if the wait was abandoned.
+__device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t, int* out_i, float* out_w, bool debug) {
+  constexpr int VPL = kMaxE / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t want = tag + P.withhold;
+  float v[VPL];
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      float s = 0.f;
+      if (e < P.E) {
+        const uint64_t* p = &P.lgp[((size_t)t * P.E + e) * kRouterParts];
+#pragma unroll
+        for (int q = 0; q < kRouterParts; ++q) {
+          const uint64_t wv = ld_tagged(p + q);
+          ok &= tag_ok(wv, want);
+          s += tag_f32(wv);
+        }
+      }
+      v[i] = s;
+    }
+    if (__all(ok)) break;
+    if (!keep_waiting(P, tag, t0)) return false;
+  }
+  if (debug) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < P.E) P.logits[(size_t)t * P.E + e] = v[i];
+    }
+  }
+  uint32_t taken = 0;
+  float my_v = 0.f, vmax = 0.f;
+  int my_i = 0;
+  for (int j = 0; j < P.k; ++j) {
+    float bv = 0.f;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < P.E && !((taken >> i) & 1u)) {
+        if (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oi = __shfl_xor(bi, off, kWave);
+      const bool better = (bi == 0x7FFFFFFF) || (oi != 0x7FFFFFFF && (ov > bv || (ov == bv && oi < bi)));
+      if (better) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (j == 0) vmax = bv;
+    if (lane == j) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float ex = (lane < P.k) ? expf(my_v - vmax) : 0.f;
+  const float z = wave_sum(ex);
+  *out_i = my_i;
+  *out_w = ex / z;
+  return true;
+}
+
+// Every workgroup computes all tokens' top-k into LDS (small batches).
+__device__ __forceinline__ bool topk_local(const Params& P, const Smem& S, uint32_t tag, bool debug) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  bool ok = true;
+  for (int t = wave; t < P.T && ok; t += kWaves) {
+    int ii;
+    float ww;
+    ok = topk_token(P, tag, t, &ii, &ww, debug);
+    if (ok && lane < P.k) {
+      S.tki[t * P.k + lane] = ii;
+      S.tkw[t * P.k + lane] = ww;
+    }
+  }
+  return ok;
+}
+
+// One wave per token across the grid; results as tagged words (large batches).
+__device__ __forceinline__ bool topk_global(const Params& P, uint32_t tag, int gw, int NW) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int t = gw; t < P.T; t += NW) {
+    int ii;
+    float ww;
+    if (!topk_token(P, tag, t, &ii, &ww, true)) return false;
+    if (lane < P.k) {
+      st_tagged(&P.tki[(size_t)t * P.k + lane], (uint32_t)ii, tag);
+      st_tagged(&P.tkw[(size_t)t * P.k + lane], __builtin_bit_cast(uint32_t, ww), tag);
+    }
+  }
+  return true;
+}
+
+// Copy all tagged top-k results into LDS (waits for them).  All threads.
+__device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32_t tag) {
+  const int TK = P.T * P.k;
+  bool ok = true;
+  const uint64_t t0 = wall_clock64();
+  for (int base = 0; base < TK && ok; base += kWG) {
+    const int s = base + threadIdx.x;
+    for (;;) {
+      bool ready = true;
+      if (s < TK) {
+        const uint64_t a = ld_tagged(&P.tki[s]), b = ld_tagged(&P.tkw[s]);
+        ready = tag_ok(a, tag) && tag_ok(b, tag);
+        if (ready) {
+          S.tki[s] = tag_i32(a);
+          S.tkw[s] = tag_f32(b);
+        }
+      }
+      if (__all(ready)) break;
+      if (!keep_waiting(P, tag, t0)) {
+        ok = false;
+        break;
+      }
+    }
+  }
+  return ok;
+}
+
+// ---------------------------------------------------------- permutation -----
+// Pairs (token t, slot j) ordered by (expert asc, token asc): one bit per
+// (expert, token) set with an LDS atomic OR (order independent); the rank of
+// a pair in its expert's list is the number of set bits below its token.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int s = scratch[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// All threads of the workgroup.  Reads S.tki / S.tkw, writes S.off / S.slot /
+// S.act / S.misc[0]; `debug` also writes the plain copies to global memory.
+__device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool debug) {
+  const int tid = threadIdx.x;
+  const int W = (P.T + 63) / 64;
+  const int E = P.E, TK = P.T * P.k;
+  uint64_t* mask = S.mask;
+  __syncthreads();
+  for (int i = tid; i < E * W; i += kWG) mask[i] = 0ull;
+  __syncthreads();
+  for (int s = tid; s < TK; s += kWG) {
+    const int t = s / P.k, e = S.tki[s];
+    atomicOr(reinterpret_cast<unsigned long long*>(&mask[(size_t)e * W + t / 64]), 1ull << (t & 63));
+  }
+  __syncthreads();
+  // counts and exclusive scans over experts, two experts per thread (E <= 1024)
+  const int e0 = tid * 2;
+  int c2[2], a2[2], csum = 0, asum = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = e0 + i;
+    int c = 0;
+    if (e < E)
+      for (int w = 0; w < W; ++w) c += __popcll(mask[(size_t)e * W + w]);
+    c2[i] = c;
+    a2[i] = c > 0;
+    csum += c;
+    asum += a2[i];
+  }
+  int ctot, atot;
+  int cbase = block_exclusive_scan(csum, S.misc + 8, &ctot);
+  int abase = block_exclusive_scan(asum, S.misc + 8, &atot);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      S.off[e] = cbase;
+      if (a2[i]) S.act[abase] = e;
+      if (debug) {
+        P.offsets[e] = cbase;
+        if (a2[i]) P.active[abase] = e;
+      }
+    }
+    cbase += c2[i];
+    abase += a2[i];
+  }
+  if (tid == 0) {
+    S.off[E] = ctot;
+    S.misc[0] = atot;
+    if (debug) {
+      P.offsets[E] = ctot;
+      *P.n_active = atot;
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < TK; s += kWG) {
+    const int t = s / P.k, e = S.tki[s];
+    const uint64_t* me = mask + (size_t)e * W;
+    int r = 0;
+    for (int w = 0; w < t / 64; ++w) r += __popcll(me[w]);
+    r += __popcll(me[t / 64] & ((1ull << (t & 63)) - 1ull));
+    const int p = S.off[e] + r;
+    S.slot[p] = s;
+    if (debug) {
+      P.pos[s] = p;
+      P.sorted_slot[p] = s;
+      P.topk_idx[s] = e;
+      P.topk_w[s] = S.tkw[s];
+    }
+  }
+  __syncthreads();
+}
+
+// ----------------------------------------------------- x into LDS -----------
+// Token rows of x in a piece-transposed layout: 16-byte piece q (elements
+// 8q..8q+7) of chunk c (elements 32c..32c+31) of row r at index
+// r*4*NCH + q*NCH + c, so lanes reading consecutive chunks hit consecutive
+// LDS addresses.  `tok(r)` maps a staged row to a token.
+template <class TokOf>
+__device__ __forceinline__ void stage_x(const Params& P, u32x4_t* xs, int nrows, TokOf tok) {
+  const int NCH = P.d / 32, per = 4 * NCH;
+  const int n = nrows * per;
+  constexpr int U = 4;
+  for (int base = 0; base < n; base += kWG * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int i = min(base + j * kWG + (int)threadIdx.x, n - 1);
+      const int r = i / per, rem = i % per, c = rem / 4, q = rem % 4;
+      v[j] = *reinterpret_cast<const u32x4_t*>(P.x + (size_t)tok(r) * P.d + (size_t)c * 32 + q * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int i = base + j * kWG + (int)threadIdx.x;
+      if (i < n) {
+        const int r = i / per, rem = i % per, c = rem / 4, q = rem % 4;
+        xs[r * per + q * NCH + c] = v[j];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- gate/up + SwiGLU ---------
+// Row pair i of expert e ([P5-FP4] gate_proj, up_proj): g = W_gate[i] . x_t,
+// u = W_up[i] . x_t for every token t routed to e, h = silu(g) * u.
+
+struct GURow {
+  u32x4_t g[kGUChunks], u[kGUChunks];
+  uint32_t sg[kGUChunks], su[kGUChunks];
+};
+
+__device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho, GURow& R) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int d = P.d, F = P.F, NCH = d / 32;
+  const int a = uni(rho / F), i = uni(rho % F);
+  const int e = uni(S.act[a]);
+  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
+  const uint8_t* pg = P.packed + (size_t)e * pbytes + (size_t)i * (d / 2);
+  const uint8_t* pu = pg + (size_t)F * d / 2;
+  const uint8_t* sg = P.scales + (size_t)e * sbytes + (size_t)i * NCH;
+  const uint8_t* su = sg + (size_t)F * NCH;
+#pragma unroll
+  for (int m = 0; m < kGUChunks; ++m) {
+    const int c = lane + kWave * m;
+    if (c < NCH) {
+      R.g[m] = ld_stream16(pg + c * 16);
+      R.u[m] = ld_stream16(pu + c * 16);
+      R.sg[m] = sg[c];
+      R.su[m] = su[c];
+    }
+  }
+}
+
+// x of token row `xrow` (piece-transposed in LDS) against a loaded row pair.
+__device__ __forceinline__ void gu_dot(const Params& P, const u32x4_t* xs, int xrow, const GURow& R, float& g,
+                                       float& u) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int NCH = P.d / 32;
+  const u32x4_t* xb = xs + (size_t)xrow * 4 * NCH;
+#pragma unroll
+  for (int m = 0; m < kGUChunks; ++m) {
+    const int c = lane + kWave * m;
+    if (c < NCH) {
+      u32x4_t xq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + c];
+      g = dot32_bf16(R.g[m], e8m0_to_f32(R.sg[m]), xq, g);
+      u = dot32_bf16(R.u[m], e8m0_to_f32(R.su[m]), xq, u);
+    }
+  }
+}
+
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// Small batches: x of every token resident in LDS (row t = token t).
+__device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem& S, uint32_t tag, int rho,
+                                                    const GURow& R) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int a = uni(rho / P.F), i = uni(rho % P.F);
+  const int e = uni(S.act[a]);
+  const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
+  for (int tt = 0; tt < ne; ++tt) {
+    const int t = uni(S.slot[p0 + tt]) / P.k;
+    float g = 0.f, u = 0.f;
+    gu_dot(P, S.xs, t, R, g, u);
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == 0) st_tagged(&P.hq[(size_t)(p0 + tt) * P.F + i], __builtin_bit_cast(uint32_t, swiglu(g, u)), tag);
+  }
+}
+
+// Each wave streams a contiguous range of the n_active*F row pairs, loading
+// the next row pair while computing the current one.
+__device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
+  const int64_t total = (int64_t)S.misc[0] * P.F;
+  const int q0 = (int)(total * gw / NW), q1 = (int)(total * (gw + 1) / NW);
+  if (q0 >= q1) return;
+  GURow A, B;
+  gu_load(P, S, q0, A);
+  for (int rho = q0; rho < q1; rho += 2) {
+    if (rho + 1 < q1) gu_load(P, S, rho + 1, B);
+    gu_compute_resident(P, S, tag, rho, A);
+    if (rho + 2 < q1) gu_load(P, S, rho + 2, A);
+    if (rho + 1 < q1) gu_compute_resident(P, S, tag, rho + 1, B);
+  }
+}
+
+// Large batches: workgroup units (active expert, kRowsGU row pairs); the
+// expert's tokens are staged into LDS P.ntl rows at a time.  All threads.
+__device__ __forceinline__ void gate_up_units(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int F = P.F;
+  const int upe = (F + kRowsGU - 1) / kRowsGU;
+  const int nunits = S.misc[0] * upe;
+  for (int u = wg; u < nunits; u += G) {
+    const int a = u / upe, tile = u % upe;
+    const int e = S.act[a];
+    const int p0 = S.off[e], ne = S.off[e + 1] - p0;
+    const int i0 = tile * kRowsGU, i1 = min(F, i0 + kRowsGU);
+    for (int tg = 0; tg < ne; tg += P.ntl) {
+      const int ntok = min(P.ntl, ne - tg);
+      __syncthreads();
+      stage_x(P, S.xs, ntok, [&](int r) { return S.slot[p0 + tg + r] / P.k; });
+      __syncthreads();
+      for (int i = i0 + wave; i < i1; i += kWaves) {
+        GURow R;
+        gu_load(P, S, a * F + i, R);
+        for (int tt = 0; tt < ntok; ++tt) {
+          float g = 0.f, uu = 0.f;
+          gu_dot(P, S.xs, tt, R, g, uu);
+          g = wave_sum(g);
+          uu = wave_sum(uu);
+          if (lane == 0)
+            st_tagged(&P.hq[(size_t)(p0 + tg + tt) * F + i], __builtin_bit_cast(uint32_t, swiglu(g, uu)), tag);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------ down ----------
+// y_r = W_down[r] . h for every token of expert e ([P5-FP4] down_proj); the
+// gated value gate * y_r goes to the token's slot row.  A lane owns MM
+// 16-byte chunks of a W_down row and the matching 32*MM values of h per token
+// (registers); each step covers kDnRows rows and up to NT tokens.
+template <int MM, int ROWS>
+struct DnRows {
+  u32x4_t w[ROWS][MM];
+  uint32_t s[ROWS][MM];
+};
+
+template <int MM, int ROWS>
+__device__ __forceinline__ void dn_load(const Params& P, int e, int r0, int nr, DnRows<MM, ROWS>& R) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int d = P.d, F = P.F, NCH = F / 32;
+  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
+  const uint8_t* pd = P.packed + (size_t)e * pbytes + (size_t)F * d + (size_t)r0 * (F / 2);
+  const uint8_t* sd = P.scales + (size_t)e * sbytes + (size_t)F * d / 16 + (size_t)r0 * NCH;
+#pragma unroll
+  for (int j = 0; j < ROWS; ++j) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const int c = lane + kWave * m;
+      if (j < nr && c < NCH) {
+        R.w[j][m] = ld_stream16(pd + (size_t)j * (F / 2) + c * 16);
+        R.s[j][m] = sd[(size_t)j * NCH + c];
+      }
+    }
+  }
+}
+
+// h of pair p into registers (the lane's chunks); waits for its tags.
+template <int MM>
+__device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, float (&h)[MM][32]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int NCH = P.F / 32;
+  const uint64_t* src = P.hq + (size_t)p * P.F;
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const int c = lane + kWave * m;
+#pragma unroll
+      for (int v = 0; v < 32; ++v) {
+        if (c < NCH) {
+          const uint64_t wv = ld_tagged(src + (size_t)c * 32 + v);
+          ok &= tag_ok(wv, tag);
+          h[m][v] = tag_f32(wv);
+        } else {
+          h[m][v] = 0.f;
+        }
+      }
+    }
+    if (__all(ok)) return true;
+    if (!keep_waiting(P, tag, t0)) return false;
+  }
+}
+
+template <int MM, int NT, int ROWS>
+__device__ __forceinline__ void dn_compute(const Params& P, const Smem& S, uint32_t tag, int p0, int ntok, int r0,
+                                           int nr, const DnRows<MM, ROWS>& R, const float (&h)[NT][MM][32]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int NCH = P.F / 32;
+  float acc[NT][kDnRows];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int j = 0; j < kDnRows; ++j) acc[tt][j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < ROWS; ++j) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const int c = lane + kWave * m;
+      if (j < nr && c < NCH) {
+        float v[32];
+        decode32_f32(R.w[j][m], e8m0_to_f32(R.s[j][m]), v);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          if (tt < ntok) acc[tt][j] = dot32(v, &h[tt][m][0], acc[tt][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    if (tt < ntok) {
+      const float s = reduce8(acc[tt]);  // lanes 8j..8j+7 hold row j
+      const int j = lane >> 3;
+      if ((lane & 7) == 0 && j < nr) {
+        const int slot = uni(S.slot[p0 + tt]);
+        st_tagged(&P.yq[(size_t)slot * P.d + r0 + j], __builtin_bit_cast(uint32_t, S.tkw[slot] * s), tag);
+      }
+    }
+  }
+}
+
+// Each wave streams a contiguous range of the n_active*d rows of W_down,
+// ROWS rows per step with the next step's rows in flight.
+template <int MM, int NT, int ROWS>
+__device__ __forceinline__ bool down_waves(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
+  const int d = P.d;
+  const int64_t total = (int64_t)S.misc[0] * d;
+  const int q0 = (int)(total * gw / NW), q1 = (int)(total * (gw + 1) / NW);
+  int rho = q0;
+  while (rho < q1) {
+    const int a = uni(rho / d);
+    const int seg_end = min(q1, (a + 1) * d);
+    const int e = uni(S.act[a]);
+    const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
+    for (int tg = 0; tg < ne; tg += NT) {
+      const int ntok = min(NT, ne - tg);
+      float h[NT][MM][32];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        if (tt < ntok) {
+          if (!dn_load_h<MM>(P, tag, p0 + tg + tt, h[tt])) return false;
+        }
+      }
+      int r = rho - a * d;
+      const int rend = seg_end - a * d;
+      DnRows<MM, ROWS> A, B;
+      dn_load<MM, ROWS>(P, e, r, min(ROWS, rend - r), A);
+      for (; r < rend; r += 2 * ROWS) {
+        const int rB = r + ROWS, rA2 = r + 2 * ROWS;
+        if (rB < rend) dn_load<MM, ROWS>(P, e, rB, min(ROWS, rend - rB), B);
+        dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, r, min(ROWS, rend - r), A, h);
+        if (rA2 < rend) dn_load<MM, ROWS>(P, e, rA2, min(ROWS, rend - rA2), A);
+        if (rB < rend) dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, rB, min(ROWS, rend - rB), B, h);
+      }
+    }
+    rho = seg_end;
+  }
+  return true;
+}
+
+template <int MM>
+__device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
+  // one token per pass keeps h, two row buffers and the decode in registers
+  return down_waves<MM, 1, (MM == 1 ? 8 : 2)>(P, S, tag, gw, NW);
+}
+
+// ---------------------------------------------------------- combine ---------
+// out[t][c] = sum over j < k of the tagged gated rows y[t*k + j][c], in slot
+// order.  Unit = (token, 64 columns), one wave.
+__device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nd = (P.d + kWave - 1) / kWave;
+  const int nunits = P.T * nd;
+  for (int u = gw; u < nunits; u += NW) {
+    const int t = u / nd, c = (u % nd) * kWave + lane;
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      bool ok = true;
+      float acc = 0.f;
+      if (c < P.d) {
+        for (int j = 0; j < P.k; ++j) {
+          const uint64_t wv = ld_tagged(&P.yq[((size_t)t * P.k + j) * P.d + c]);
+          ok &= tag_ok(wv, tag);
+          acc += tag_f32(wv);
+        }
+      }
+      if (__all(ok)) {
+        if (c < P.d) P.out[(size_t)t * P.d + c] = acc;
+        break;
+      }
+      if (!keep_waiting(P, tag, t0)) return false;
+    }
+  }
+  return true;
+}
+
+// ---------------------------------------------------------- kernels ---------
+
+// The whole layer in one launch.  SMALL: x of all tokens resident in LDS and
+// top-k computed redundantly in every workgroup.  MM: W_down chunks per lane.
+template <bool SMALL, int MM>
+__global__ void __launch_bounds__(kWG) k_layer(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_ok;
+  const Smem S = carve(smem, P, SMALL, SMALL ? 0 : P.ntl);
+  const int wg = blockIdx.x, G = gridDim.x;
+  const int gw = wg * kWaves + uni(threadIdx.x / kWave), NW = G * kWaves;
+  const uint32_t tag = start_call(P, wg, true);
+  if (threadIdx.x == 0) s_ok = 1;
+  router_step(P, tag, gw, NW);
+  bool ok;
+  if (SMALL) {
+    stage_x(P, S.xs, P.T, [](int r) { return r; });
+    ok = topk_local(P, S, tag, wg == 0);
+  } else {
+    ok = topk_global(P, tag, gw, NW);
+    __syncthreads();
+    ok = load_topk(P, S, tag) && ok;
+  }
+  __syncthreads();
+  if (!ok) s_ok = 0;
+  __syncthreads();
+  if (s_ok) {
+    build_perm(P, S, wg == 0);
+    if (SMALL)
+      gate_up_waves(P, S, tag, gw, NW);
+    else
+      gate_up_units(P, S, tag, wg, G);
+    if (down_dispatch<MM>(P, S, tag, gw, NW)) combine_step(P, tag, gw, NW);
+  }
+  __syncthreads();
+  if (wg == 0) end_call(P, tag, G);
+}
+
+// One launch per step (the per-operator model), same arithmetic.
+__global__ void __launch_bounds__(kWG) k_st_router(Params P) {
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  router_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+}
+__global__ void __launch_bounds__(kWG) k_st_topk(Params P) {
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  topk_global(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+}
+__global__ void __launch_bounds__(kWG) k_st_perm(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_ok;
+  const Smem S = carve(smem, P, false, 0);
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  if (threadIdx.x == 0) s_ok = 1;
+  __syncthreads();
+  if (!load_topk(P, S, tag)) s_ok = 0;
+  __syncthreads();
+  if (s_ok) build_perm(P, S, true);
+}
+template <bool SMALL>
+__global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_ok;
+  const Smem S = carve(smem, P, SMALL, SMALL ? 0 : P.ntl);
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  if (threadIdx.x == 0) s_ok = 1;
+  __syncthreads();
+  if (!load_topk(P, S, tag)) s_ok = 0;
+  __syncthreads();
+  if (!s_ok) return;
+  build_perm(P, S, false);
+  if (SMALL) {
+    stage_x(P, S.xs, P.T, [](int r) { return r; });
+    __syncthreads();
+    gate_up_waves(P, S, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+  } else {
+    gate_up_units(P, S, tag, blockIdx.x, gridDim.x);
+  }
+}
+template <int MM>
+__global__ void __launch_bounds__(kWG) k_st_down(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_ok;
+  const Smem S = carve(smem, P, false, 0);
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  if (threadIdx.x == 0) s_ok = 1;
+  __syncthreads();
+  if (!load_topk(P, S, tag)) s_ok = 0;
+  __syncthreads();
+  if (!s_ok) return;
+  build_perm(P, S, false);
+  down_dispatch<MM>(P, S, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+}
+__global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
+  const uint32_t tag = start_call(P, blockIdx.x, false);
+  combine_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+}
+__global__ void k_st_bump(Params P) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const uint32_t e = ld_relaxed(&P.hdr[kEpoch]);
+    st_relaxed(&P.hdr[kEpoch], next_epoch(e + 1u));
+  }
+}
+__global__ void k_zero(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ------------------------------------------------------------ host side -----
+
+constexpr size_t kAlign = 256;
+static inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+static int check_dims(const moe_mxfp4_dims* dm, int32_t topk) {
+  if (!dm) return MOE_EINVAL;
+  if (dm->T < 0 || dm->E < 1 || topk < 1 || topk > dm->E) return MOE_EINVAL;
+  if (dm->E > kMaxE || topk > kMaxK) return MOE_ESHAPE;
+  if (dm->d < 32 || dm->ffn < 32 || dm->d % 32 || dm->ffn % 32) return MOE_ESHAPE;
+  if (dm->d > kMaxD || dm->ffn > kMaxF) return MOE_ESHAPE;
+  const int64_t W = ((int64_t)dm->T + 63) / 64;
+  if ((int64_t)dm->E * W > kMaxMaskWords) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t hdr, lgp, tki, tkw, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, total;
+};
+
+static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
+  Layout L;
+  const size_t T = (size_t)dm->T, E = (size_t)dm->E, TK = T * (size_t)k;
+  size_t o = 0;
+  L.hdr = o; o = align_up(o + kHdrBytes);
+  L.lgp = o; o = align_up(o + T * E * kRouterParts * 8);
+  L.tki = o; o = align_up(o + TK * 8);
+  L.tkw = o; o = align_up(o + TK * 8);
+  L.hq = o; o = align_up(o + TK * (size_t)dm->ffn * 8);
+  L.yq = o; o = align_up(o + TK * (size_t)dm->d * 8);
+  L.logits = o; o = align_up(o + T * E * 4);
+  L.topk_idx = o; o = align_up(o + TK * 4);
+  L.topk_w = o; o = align_up(o + TK * 4);
+  L.offsets = o; o = align_up(o + (E + 1) * 4);
+  L.sorted_slot = o; o = align_up(o + TK * 4);
+  L.pos = o; o = align_up(o + TK * 4);
+  L.active = o; o = align_up(o + E * 4);
+  L.n_active = o; o = align_up(o + 4);
+  L.total = o;
+  return L;
+}
+
+// x of all tokens fits in LDS next to the permutation tables.
+static bool use_small(const moe_mxfp4_dims* dm, int32_t k) {
+  return lds_plan(dm->T, dm->d, dm->E, k, true, 0).total <= (size_t)kLdsMax;
+}
+
+static int tokens_per_pass(const moe_mxfp4_dims* dm, int32_t k) {
+  const size_t fixed = lds_plan(dm->T, 32, dm->E, k, false, 0).total;  // tables (+ mask) only
+  if (fixed + (size_t)dm->d * 2 > (size_t)kLdsMax) return 0;
+  int n = (int)(((size_t)kLdsMax - fixed) / ((size_t)dm->d * 2));
+  return n > kMaxTokLds ? kMaxTokLds : n;
+}
+
+struct DeviceInfo {
+  int cus = 0;
+  uint64_t ticks_per_us = 100;
+  bool ok = false;
+};
+
+static std::mutex g_mu;
+static DeviceInfo g_info[64];
+
+static const void* layer_kernel(bool small, int mm) {
+  if (small) return mm == 1 ? (const void*)k_layer<true, 1> : (const void*)k_layer<true, 2>;
+  return mm == 1 ? (const void*)k_layer<false, 1> : (const void*)k_layer<false, 2>;
+}
+
+static int device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& di = g_info[dev];
+  if (!di.ok) {
+    int cus = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_EDEVICE;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_EDEVICE;
+    const void* ks[] = {layer_kernel(true, 1), layer_kernel(true, 2), layer_kernel(false, 1), layer_kernel(false, 2),
+                        (const void*)k_st_perm, (const void*)k_st_gate_up<true>, (const void*)k_st_gate_up<false>,
+                        (const void*)k_st_down<1>, (const void*)k_st_down<2>};
+    for (const void* f : ks) {
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess) {
+        (void)hipGetLastError();  // do not leave a sticky error for the caller's next HIP call
+        return MOE_EDEVICE;
+      }
+    }
+    di.cus = cus;
+    di.ticks_per_us = khz >= 1000 ? (uint64_t)khz / 1000u : 100u;
+    di.ok = true;
+  }
+  *out = di;
+  return MOE_OK;
+}
+
+static int check_ptrs(const void* x, const float* wr, const uint8_t* packed, const uint8_t* scales, const float* out,
+                      const void* ws) {
+  if (!x || !wr || !packed || !scales || !out || !ws) return MOE_EINVAL;
+  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
+  if (!al(x, 16) || !al(wr, 16) || !al(packed, 16) || !al(out, 16) || !al(ws, kAlign)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, const float* wr, const uint8_t* packed,
+                          const uint8_t* scales, float* out, void* ws, const DeviceInfo& di, uint32_t spin_us) {
+  const Layout L = make_layout(dm, k);
+  char* b = static_cast<char*>(ws);
+  Params P;
+  P.T = dm->T;
+  P.d = dm->d;
+  P.F = dm->ffn;
+  P.E = dm->E;
+  P.k = k;
+  P.x = static_cast<const uint16_t*>(x);
+  P.wr = wr;
+  P.packed = packed;
+  P.scales = scales;
+  P.out = out;
+  P.hdr = reinterpret_cast<uint32_t*>(b + L.hdr);
+  P.lgp = reinterpret_cast<uint64_t*>(b + L.lgp);
+  P.tki = reinterpret_cast<uint64_t*>(b + L.tki);
+  P.tkw = reinterpret_cast<uint64_t*>(b + L.tkw);
+  P.hq = reinterpret_cast<uint64_t*>(b + L.hq);
+  P.yq = reinterpret_cast<uint64_t*>(b + L.yq);
+  P.logits = reinterpret_cast<float*>(b + L.logits);
+  P.topk_idx = reinterpret_cast<int32_t*>(b + L.topk_idx);
+  P.topk_w = reinterpret_cast<float*>(b + L.topk_w);
+  P.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  P.sorted_slot = reinterpret_cast<int32_t*>(b + L.sorted_slot);
+  P.pos = reinterpret_cast<int32_t*>(b + L.pos);
+  P.active = reinterpret_cast<int32_t*>(b + L.active);
+  P.n_active = reinterpret_cast<int32_t*>(b + L.n_active);
+  const uint64_t us = spin_us ? spin_us : 2000000u;
+  P.spin_ticks = us * di.ticks_per_us;
+  P.withhold = 0;
+  P.ntl = tokens_per_pass(dm, k);
+  return P;
+}
+
+static int chunks_per_lane_down(const moe_mxfp4_dims* dm) { return (dm->ffn / 32 + kWave - 1) / kWave; }
+
+static int grid_for(const DeviceInfo& di, const void* kern, size_t lds, int requested) {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kWG, lds) != hipSuccess || occ < 1) {
+    (void)hipGetLastError();
+    occ = 1;
+  }
+  int maxg = di.cus * occ;
+  if (maxg > kMaxGrid) maxg = kMaxGrid;
+  int g = di.cus < maxg ? di.cus : maxg;  // one workgroup per CU
+  if (requested > 0) g = requested < maxg ? requested : maxg;
+  return g < 1 ? 1 : g;
+}
+
+struct Launch {
+  bool small;
+  int mm;
+  size_t lds;
+};
+
+static int plan_launch(const moe_mxfp4_dims* dm, int32_t k, Launch* L) {
+  L->small = use_small(dm, k);
+  L->mm = chunks_per_lane_down(dm);
+  if (L->mm < 1 || L->mm > 2) return MOE_ESHAPE;
+  const int ntl = tokens_per_pass(dm, k);
+  if (!L->small && ntl < 1) return MOE_ESHAPE;
+  const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->small, L->small ? 0 : ntl);
+  if (pl.total > (size_t)kLdsMax) return MOE_ESHAPE;
+  L->lds = pl.total;
+  return MOE_OK;
+}
+
+static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s) {
+  void* args[] = {&P};
+  hipError_t e = hipLaunchCooperativeKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args,
+                                            (unsigned)L.lds, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  return MOE_OK;
+}
+
+static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t s, bool experts) {
+  const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, false, 0).total;
+  hipLaunchKernelGGL(k_st_router, dim3(grid), dim3(kWG), 0, s, P);
+  hipLaunchKernelGGL(k_st_topk, dim3(grid), dim3(kWG), 0, s, P);
+  if (experts) {
+    if (L.small)
+      hipLaunchKernelGGL(k_st_gate_up<true>, dim3(grid), dim3(kWG), (unsigned)L.lds, s, P);
+    else
+      hipLaunchKernelGGL(k_st_gate_up<false>, dim3(grid), dim3(kWG), (unsigned)L.lds, s, P);
+    if (L.mm == 1)
+      hipLaunchKernelGGL(k_st_down<1>, dim3(grid), dim3(kWG), lds_tables, s, P);
+    else
+      hipLaunchKernelGGL(k_st_down<2>, dim3(grid), dim3(kWG), lds_tables, s, P);
+    hipLaunchKernelGGL(k_st_combine, dim3(grid), dim3(kWG), 0, s, P);
+  }
+  // the permutation copies for inspection come from one workgroup
+  hipLaunchKernelGGL(k_st_perm, dim3(1), dim3(kWG), lds_tables, s, P);
+  hipLaunchKernelGGL(k_st_bump, dim3(1), dim3(64), 0, s, P);
+  if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_mxfp4_expert_packed_bytes(int32_t d, int32_t ffn) {
+  if (d <= 0 || ffn <= 0) return 0;
+  return (size_t)3 * (size_t)d * (size_t)ffn / 2;
+}
+
+size_t moe_mxfp4_expert_scale_bytes(int32_t d, int32_t ffn) {
+  if (d <= 0 || ffn <= 0) return 0;
+  return (size_t)3 * (size_t)d * (size_t)ffn / 32;
+}
+
+size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_dims* dims, int32_t topk) {
+  if (check_dims(dims, topk) != MOE_OK) return 0;
+  return make_layout(dims, topk).total;
+}
+
+int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxfp4_ws_layout* out) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_EINVAL;
+  const Layout L = make_layout(dims, topk);
+  out->logits = L.logits;
+  out->topk_idx = L.topk_idx;
+  out->topk_w = L.topk_w;
+  out->offsets = L.offsets;
+  out->sorted_slot = L.sorted_slot;
+  out->pos = L.pos;
+  out->active = L.active;
+  out->n_active = L.n_active;
+  out->h = L.hq;
+  out->y = L.yq;
+  out->total = L.total;
+  return MOE_OK;
+}
+
+int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return MOE_EINVAL;
+  if (workspace_bytes < kHdrBytes) return MOE_EWORKSPACE;
+  if ((uintptr_t)workspace % kAlign) return MOE_EALIGN;
+  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, (hipStream_t)stream, (uint4*)workspace,
+                     workspace_bytes / 16);
+  if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+  return MOE_OK;
+}
+
+int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return -st;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return -st;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MOE_OK) return -st;
+  return grid_for(di, layer_kernel(L.small, L.mm), L.lds, 0);
+}
+
+int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                         const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                         void* workspace, size_t workspace_bytes, const moe_mxfp4_options* opts, void* stream) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (opts && (opts->flags & ~MOE_OPT_WITHHOLD_ARRIVAL)) return MOE_EINVAL;
+  if (opts && opts->grid < 0) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;  // nothing to do; buffers may be empty (null)
+  st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
+  if (st != MOE_OK) return st;
+  if (workspace_bytes < make_layout(dims, topk).total) return MOE_EWORKSPACE;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return st;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MOE_OK) return st;
+  Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di,
+                         opts ? opts->spin_limit_us : 0u);
+  if (opts && (opts->flags & MOE_OPT_WITHHOLD_ARRIVAL)) P.withhold = 1;
+  const int grid = grid_for(di, layer_kernel(L.small, L.mm), L.lds, opts ? opts->grid : 0);
+  return launch_layer(P, L, grid, (hipStream_t)stream);
+}
+
+int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                      const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_mxfp4_forward_ex(dims, x, router_w, packed_experts, scales, topk, out, workspace, workspace_bytes,
+                              nullptr, stream);
+}
+
+int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                             const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
+  if (st != MOE_OK) return st;
+  if (workspace_bytes < make_layout(dims, topk).total) return MOE_EWORKSPACE;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return st;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MOE_OK) return st;
+  Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di, 0u);
+  return launch_staged(P, L, di.cus, (hipStream_t)stream, true);
+}
+
+int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* router_w, int32_t topk,
+                    int32_t* topk_idx, float* topk_w, int32_t* expert_offsets, int32_t* sorted_slot, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !router_w || !workspace) return MOE_EINVAL;
+  if ((uintptr_t)x % 16 || (uintptr_t)router_w % 16 || (uintptr_t)workspace % kAlign) return MOE_EALIGN;
+  if (workspace_bytes < make_layout(dims, topk).total) return MOE_EWORKSPACE;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return st;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MOE_OK) return st;
+  // packed/scales/out are not touched by the routing kernels
+  Params P = make_params(dims, topk, x, router_w, nullptr, nullptr, nullptr, workspace, di, 0u);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_staged(P, L, di.cus, s, false);
+  if (st != MOE_OK) return st;
+  const size_t TK = (size_t)dims->T * topk;
+  if (topk_idx && hipMemcpyAsync(topk_idx, P.topk_idx, TK * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_EDEVICE;
+  if (topk_w && hipMemcpyAsync(topk_w, P.topk_w, TK * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_EDEVICE;
+  if (expert_offsets &&
+      hipMemcpyAsync(expert_offsets, P.offsets, ((size_t)dims->E + 1) * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_EDEVICE;
+  if (sorted_slot && hipMemcpyAsync(sorted_slot, P.sorted_slot, TK * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_EDEVICE;
+  return MOE_OK;
+}
+
+int moe_mxfp4_status(void* workspace, void* stream) {
+  if (!workspace) return MOE_EINVAL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_EDEVICE;
+  uint32_t st = 0;
+  uint32_t* w = reinterpret_cast<uint32_t*>(workspace) + kStatus;
+  if (hipMemcpy(&st, w, 4, hipMemcpyDeviceToHost) != hipSuccess) return MOE_EDEVICE;
+  const uint32_t zero = 0;
+  if (hipMemcpy(w, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return MOE_EDEVICE;
+  return (int)st;
+}
+
+const char* moe_mxfp4_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ESHAPE: return "unsupported shape";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_ETIMEOUT: return "device wait timed out";
+    case MOE_EDEVICE: return "device query or copy failed";
+    case MOE_EALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -308,7 +308,10 @@ double oracle_forward(int T, int d, int F, int E, int k, const uint16_t* x, cons
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
   for (int e = 0; e < E; ++e) {
-    if (offsets[e + 1] == offsets[e]) continue;
+    int used = 0; /* skip experts none of whose tokens is requested */
+    for (int32_t p = offsets[e]; p < offsets[e + 1] && !used; ++p)
+      used = !token_mask || token_mask[sslot[p] / k];
+    if (!used) continue;
     expert_apply(packed + e * pbytes, scales + e * sbytes, d, F, xd, sslot, k, token_mask,
                  offsets[e], offsets[e + 1], h, y);
   }

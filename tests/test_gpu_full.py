@@ -1,0 +1,85 @@
+"""GPU parity at the layer's full workload sizes (d=7168, ffn=2048, E=256,
+top-8), in the launch configuration the benchmark times (the persistent
+single launch with its default grid).
+
+decode (T=1) and verify (T=8): every output element against the oracle.
+batched_verify (T=128, Zipf-skewed routing) and dense (T=512): routing and
+permutation for all tokens, outputs for a sample of tokens (the oracle runs
+only those tokens' expert pairs).
+"""
+import numpy as np
+import pytest
+
+from helpers import OUT_TOL, check_routing, rel_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def full_env():
+    import torch
+
+    import mxfp4_moe_expert_router_amd as moe
+    from oracle import oracle
+    from synth import synth
+
+    oracle.build()
+    synth.build()
+    cfg = synth.get_config("verify")
+    print("\n[full] generating 256 MXFP4 experts (d=7168, ffn=2048)", flush=True)
+    p, s = synth.expert_weights(cfg)
+    pt = torch.from_numpy(p).cuda()
+    st = torch.from_numpy(s).cuda()
+    torch.cuda.synchronize()
+    print("[full] experts resident on the GPU", flush=True)
+    return torch, moe, oracle, synth, p, s, pt, st
+
+
+def _run(full_env, name, sample=None):
+    torch, moe, oracle, synth, p, s, pt, st = full_env
+    cfg = synth.get_config(name)
+    print(f"\n[full] {name}: T={cfg.T} route_seed={cfg.route_seed}", flush=True)
+    x, wr = synth.routing_inputs(cfg)
+    mask = None
+    if sample is not None:
+        mask = np.zeros(cfg.T, dtype=np.uint8)
+        mask[sample] = 1
+    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F, token_mask=mask)
+    assert ref.min_gap > 1e-3
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wrt = torch.from_numpy(wr).cuda()
+    dims = moe.LayerDims(cfg.T, cfg.d, cfg.F, cfg.E)
+    ws = moe.alloc_workspace(dims, cfg.k)
+    out = moe.forward(xt, wrt, pt, st, cfg.k, workspace=ws, dims=dims)
+    torch.cuda.synchronize()
+    assert moe.status(ws) == moe.MOE_OK
+    it = {k: v.cpu().numpy() for k, v in moe.intermediates(ws, dims, cfg.k).items()}
+    check_routing(it["topk_idx"], it["topk_w"], it["offsets"], it["sorted_slot"], ref, cfg.k)
+    got = out.cpu().numpy()
+    rows = np.arange(cfg.T) if sample is None else np.asarray(sample)
+    err = rel_err(got[rows], ref.out[rows])
+    print(f"[full] {name}: active experts {int((np.diff(ref.offsets) > 0).sum())}, out err {err:.2e}", flush=True)
+    assert err <= OUT_TOL
+    # staged path gives the same bits
+    out2 = moe.forward(xt, wrt, pt, st, cfg.k, workspace=ws, dims=dims, staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    return got, ref
+
+
+def test_decode_T1(full_env):
+    _run(full_env, "decode")
+
+
+def test_verify_T8(full_env):
+    _run(full_env, "verify")
+
+
+def test_batched_verify_T128_zipf(full_env):
+    got, ref = _run(full_env, "batched_verify", sample=[0, 17, 40, 63, 64, 99, 127])
+    counts = np.diff(ref.offsets)
+    assert 35 <= counts.max() <= 45 and (counts == 0).any()
+
+
+def test_dense_T512(full_env):
+    _run(full_env, "dense", sample=[0, 1, 255, 256, 300, 511])
