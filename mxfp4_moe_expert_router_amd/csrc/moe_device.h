@@ -90,6 +90,11 @@ __device__ __forceinline__ u32x4_t ld_stream16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
+// Bits -> float through a by-value parameter.  (Do not write
+// __builtin_bit_cast(float, v.z) on an ext_vector element: this toolchain
+// lowers it as a read of element 0.)
+__device__ __forceinline__ float u2f(uint32_t v) { return __builtin_bit_cast(float, v); }
+
 // Value known to be equal in all lanes of the wave, moved to a scalar register.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -196,6 +201,20 @@ __device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+// Buffer descriptor over `bytes` bytes at `base` (a wave-uniform address);
+// reads past the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte agent-coherent load (sc1: not served from a stale L2 line of
+// another call) of two tagged words {lo value, lo tag, hi value, hi tag}.
+// Each aligned 8-byte half is read single-copy atomically.  Unlike atomic
+// loads, several of these stay in flight at once.
+__device__ __forceinline__ u32x4_t ld_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
+}
 __device__ __forceinline__ float tag_f32(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
 __device__ __forceinline__ int tag_i32(uint64_t w) { return (int)(uint32_t)w; }
 

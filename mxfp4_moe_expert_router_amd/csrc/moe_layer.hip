@@ -78,7 +78,7 @@ constexpr int kMaxGrid = 2048;
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
 
 // Header words (first kHdrBytes of the workspace).
-enum { kEpoch = 0, kStatus = 1, kAbort = 2, kStarted = 64 };
+enum { kEpoch = 0, kStatus = 1, kAbort = 2, kWhere = 3, kWhat = 4, kStarted = 64 };
 constexpr size_t kHdrBytes = (size_t)(kStarted + kMaxGrid) * 4;
 
 struct Params {
@@ -173,19 +173,33 @@ __device__ __forceinline__ bool aborted(const Params& P, uint32_t tag) {
   return ld_relaxed(&P.hdr[kAbort]) == tag;
 }
 
-__device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag) {
+// Wait sites, recorded with the index waited on when a watchdog fires.
+enum { kSiteLogits = 1, kSiteTopk = 2, kSiteH = 3, kSiteY = 4, kSiteStarted = 5 };
+
+__device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag, uint32_t site, uint32_t what) {
+  st_relaxed(&P.hdr[kWhere], site);
+  st_relaxed(&P.hdr[kWhat], what);
   st_relaxed(&P.hdr[kStatus], (uint32_t)MOE_ETIMEOUT);
   st_relaxed(&P.hdr[kAbort], tag);
 }
 
 // One spin round of a wave-level wait: true to retry, false to give up.
-__device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint64_t t0) {
+// Rounds back off exponentially (about 0.5 us doubling to 8 us) so that waves
+// that wait do not flood the memory system that the waves they wait for are
+// using.  The compiler memory barrier makes the caller's polling loads (plain
+// buffer loads, not atomics) be issued again on the next round instead of
+// being reused from registers.
+__device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint64_t t0, uint32_t site,
+                                             uint32_t what, int& round) {
   if (aborted(P, tag)) return false;
   if (wall_clock64() - t0 > P.spin_ticks) {
-    raise_timeout(P, tag);
+    raise_timeout(P, tag, site, what);
     return false;
   }
-  __builtin_amdgcn_s_sleep(2);
+  const int units = 1 << min(round, 4);
+  for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(20);
+  ++round;
+  __asm__ __volatile__("" ::: "memory");
   return true;
 }
 
@@ -210,12 +224,13 @@ __device__ __forceinline__ void end_call(const Params& P, uint32_t tag, int G) {
   const int lane = threadIdx.x & (kWave - 1);
   if (threadIdx.x < kWave) {
     const uint64_t t0 = wall_clock64();
+  int round = 0;
     for (;;) {
       bool ok = true;
       for (int w = lane; w < G; w += kWave) ok &= (ld_relaxed(&P.hdr[kStarted + w]) == tag);
       if (__all(ok)) break;
       if (wall_clock64() - t0 > P.spin_ticks) {
-        if (lane == 0) raise_timeout(P, tag);
+        if (lane == 0) raise_timeout(P, tag, kSiteStarted, 0);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -241,12 +256,15 @@ __device__ __forceinline__ void router_step(const Params& P, uint32_t tag, int g
     const int e = u / (ngr * kRouterParts);
     const int t0 = g * kRouterTok, nt = min(kRouterTok, P.T - t0);
     const int c0 = part * dp;
-    const float4* w = reinterpret_cast<const float4*>(P.wr + (size_t)e * P.d + c0);
-    float4 wv[kRouterF4];
+    const f32x4_t* w = reinterpret_cast<const f32x4_t*>(P.wr + (size_t)e * P.d + c0);
+    f32x4_t wv[kRouterF4];
 #pragma unroll
     for (int i = 0; i < kRouterF4; ++i) {
-      const int c = lane + kWave * i;
-      wv[i] = (c < n4) ? w[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kWave * i < n4) {  // uniform; the tail lanes read a valid chunk and get a zero weight
+        const int c = lane + kWave * i;
+        const f32x4_t v = w[min(c, n4 - 1)];
+        wv[i] = c < n4 ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
     float acc[kRouterTok];
 #pragma unroll
@@ -256,8 +274,8 @@ __device__ __forceinline__ void router_step(const Params& P, uint32_t tag, int g
         const uint16_t* xt = P.x + (size_t)(t0 + j) * P.d + c0;
 #pragma unroll
         for (int i = 0; i < kRouterF4; ++i) {
-          const int c = lane + kWave * i;
-          if (c < n4) {
+          if (kWave * i < n4) {
+            const int c = min(lane + kWave * i, n4 - 1);
             const uint2 xv = *reinterpret_cast<const uint2*>(xt + (size_t)c * 4);
             acc[j] = fmaf(wv[i].x, bf16lo(xv.x), acc[j]);
             acc[j] = fmaf(wv[i].y, bf16hi(xv.x), acc[j]);
@@ -286,26 +304,26 @@ __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t,
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t want = tag + P.withhold;
   float v[VPL];
+  static_assert(kRouterParts == 2, "one 16-byte load holds the two partial logits of an expert");
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.lgp + (size_t)t * P.E * kRouterParts, P.E * kRouterParts * 8);
   const uint64_t t0 = wall_clock64();
+  int round = 0;
   for (;;) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      float s = 0.f;
-      if (e < P.E) {
-        const uint64_t* p = &P.lgp[((size_t)t * P.E + e) * kRouterParts];
-#pragma unroll
-        for (int q = 0; q < kRouterParts; ++q) {
-          const uint64_t wv = ld_tagged(p + q);
-          ok &= tag_ok(wv, want);
-          s += tag_f32(wv);
+      v[i] = 0.f;
+      if (kWave * i < P.E) {  // uniform
+        const int e = lane + kWave * i;
+        const u32x4_t q = ld_coherent16(rs, (uint32_t)min(e, P.E - 1) * 16u);
+        if (e < P.E) {
+          ok &= (q.y == want) && (q.w == want);
+          v[i] = u2f(q.x) + u2f(q.z);
         }
       }
-      v[i] = s;
     }
     if (__all(ok)) break;
-    if (!keep_waiting(P, tag, t0)) return false;
+    if (!keep_waiting(P, tag, t0, kSiteLogits, t, round)) return false;
   }
   if (debug) {
 #pragma unroll
@@ -390,6 +408,7 @@ __device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32
   const int TK = P.T * P.k;
   bool ok = true;
   const uint64_t t0 = wall_clock64();
+  int round = 0;
   for (int base = 0; base < TK && ok; base += kWG) {
     const int s = base + threadIdx.x;
     for (;;) {
@@ -403,7 +422,7 @@ __device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32
         }
       }
       if (__all(ready)) break;
-      if (!keep_waiting(P, tag, t0)) {
+      if (!keep_waiting(P, tag, t0, kSiteTopk, base, round)) {
         ok = false;
         break;
       }
@@ -544,6 +563,9 @@ struct GURow {
   uint32_t sg[kGUChunks], su[kGUChunks];
 };
 
+// Loads are unconditional (no divergent branch between them, so they all stay
+// in flight): a lane past the end of the row re-reads the row's last chunk and
+// gets a zero scale, which decodes its codes to 0.
 __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho, GURow& R) {
   const int lane = threadIdx.x & (kWave - 1);
   const int d = P.d, F = P.F, NCH = d / 32;
@@ -557,12 +579,12 @@ __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho,
 #pragma unroll
   for (int m = 0; m < kGUChunks; ++m) {
     const int c = lane + kWave * m;
-    if (c < NCH) {
-      R.g[m] = ld_stream16(pg + c * 16);
-      R.u[m] = ld_stream16(pu + c * 16);
-      R.sg[m] = sg[c];
-      R.su[m] = su[c];
-    }
+    const int cc = min(c, NCH - 1);
+    R.g[m] = ld_stream16(pg + cc * 16);
+    R.u[m] = ld_stream16(pu + cc * 16);
+    const uint32_t keep = c < NCH ? 0xFFu : 0u;
+    R.sg[m] = sg[cc] & keep;
+    R.su[m] = su[cc] & keep;
   }
 }
 
@@ -574,11 +596,11 @@ __device__ __forceinline__ void gu_dot(const Params& P, const u32x4_t* xs, int x
   const u32x4_t* xb = xs + (size_t)xrow * 4 * NCH;
 #pragma unroll
   for (int m = 0; m < kGUChunks; ++m) {
-    const int c = lane + kWave * m;
-    if (c < NCH) {
+    if (kWave * m < NCH) {  // uniform
+      const int cc = min(lane + kWave * m, NCH - 1);
       u32x4_t xq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + c];
+      for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + cc];
       g = dot32_bf16(R.g[m], e8m0_to_f32(R.sg[m]), xq, g);
       u = dot32_bf16(R.u[m], e8m0_to_f32(R.su[m]), xq, u);
     }
@@ -613,9 +635,9 @@ __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, ui
   GURow A, B;
   gu_load(P, S, q0, A);
   for (int rho = q0; rho < q1; rho += 2) {
-    if (rho + 1 < q1) gu_load(P, S, rho + 1, B);
+    gu_load(P, S, min(rho + 1, q1 - 1), B);  // the last odd step re-reads a row it does not use
     gu_compute_resident(P, S, tag, rho, A);
-    if (rho + 2 < q1) gu_load(P, S, rho + 2, A);
+    gu_load(P, S, min(rho + 2, q1 - 1), A);
     if (rho + 1 < q1) gu_compute_resident(P, S, tag, rho + 1, B);
   }
 }
@@ -674,13 +696,13 @@ __device__ __forceinline__ void dn_load(const Params& P, int e, int r0, int nr, 
   const uint8_t* sd = P.scales + (size_t)e * sbytes + (size_t)F * d / 16 + (size_t)r0 * NCH;
 #pragma unroll
   for (int j = 0; j < ROWS; ++j) {
+    const int jj = min(j, nr - 1);  // rows past the end re-read the last row (not stored)
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
       const int c = lane + kWave * m;
-      if (j < nr && c < NCH) {
-        R.w[j][m] = ld_stream16(pd + (size_t)j * (F / 2) + c * 16);
-        R.s[j][m] = sd[(size_t)j * NCH + c];
-      }
+      const int cc = min(c, NCH - 1);
+      R.w[j][m] = ld_stream16(pd + (size_t)jj * (F / 2) + cc * 16);
+      R.s[j][m] = sd[(size_t)jj * NCH + cc] & (c < NCH ? 0xFFu : 0u);
     }
   }
 }
@@ -690,26 +712,31 @@ template <int MM>
 __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, float (&h)[MM][32]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int NCH = P.F / 32;
-  const uint64_t* src = P.hq + (size_t)p * P.F;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq + (size_t)p * P.F, (uint32_t)P.F * 8u);
   const uint64_t t0 = wall_clock64();
+  int round = 0;
+  // cheap pre-check first: two words per lane spread over the F rows (512 B
+  // per wave per round instead of the whole 8*F bytes)
+  const uint32_t probe = (uint32_t)min((lane * P.F / kWave) & ~1, P.F - 2) * 8u;
   for (;;) {
-    bool ok = true;
+    const u32x4_t q = ld_coherent16(rs, probe);
+    if (__all((q.y == tag) && (q.w == tag))) {
+      bool ok = true;
 #pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      const int c = lane + kWave * m;
+      for (int m = 0; m < MM; ++m) {
+        const int c = lane + kWave * m;
+        const uint32_t base = (uint32_t)min(c, NCH - 1) * 256u;  // 32 tagged words per chunk
 #pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        if (c < NCH) {
-          const uint64_t wv = ld_tagged(src + (size_t)c * 32 + v);
-          ok &= tag_ok(wv, tag);
-          h[m][v] = tag_f32(wv);
-        } else {
-          h[m][v] = 0.f;
+        for (int v = 0; v < 16; ++v) {
+          const u32x4_t w = ld_coherent16(rs, base + v * 16u);
+          ok &= (w.y == tag) && (w.w == tag);
+          h[m][2 * v] = c < NCH ? u2f(w.x) : 0.f;
+          h[m][2 * v + 1] = c < NCH ? u2f(w.z) : 0.f;
         }
       }
+      if (__all(ok)) return true;
     }
-    if (__all(ok)) return true;
-    if (!keep_waiting(P, tag, t0)) return false;
+    if (!keep_waiting(P, tag, t0, kSiteH, p, round)) return false;
   }
 }
 
@@ -727,8 +754,7 @@ __device__ __forceinline__ void dn_compute(const Params& P, const Smem& S, uint3
   for (int j = 0; j < ROWS; ++j) {
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-      const int c = lane + kWave * m;
-      if (j < nr && c < NCH) {
+      if (kWave * m < NCH) {  // uniform; lanes past the row end have scale 0 and h 0
         float v[32];
         decode32_f32(R.w[j][m], e8m0_to_f32(R.s[j][m]), v);
 #pragma unroll
@@ -777,11 +803,12 @@ __device__ __forceinline__ bool down_waves(const Params& P, const Smem& S, uint3
       DnRows<MM, ROWS> A, B;
       dn_load<MM, ROWS>(P, e, r, min(ROWS, rend - r), A);
       for (; r < rend; r += 2 * ROWS) {
-        const int rB = r + ROWS, rA2 = r + 2 * ROWS;
-        if (rB < rend) dn_load<MM, ROWS>(P, e, rB, min(ROWS, rend - rB), B);
+        // prefetches past the segment end re-read its last row and are not used
+        const int rB = min(r + ROWS, rend - 1), rA2 = min(r + 2 * ROWS, rend - 1);
+        dn_load<MM, ROWS>(P, e, rB, min(ROWS, rend - rB), B);
         dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, r, min(ROWS, rend - r), A, h);
-        if (rA2 < rend) dn_load<MM, ROWS>(P, e, rA2, min(ROWS, rend - rA2), A);
-        if (rB < rend) dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, rB, min(ROWS, rend - rB), B, h);
+        dn_load<MM, ROWS>(P, e, rA2, min(ROWS, rend - rA2), A);
+        if (r + ROWS < rend) dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, r + ROWS, min(ROWS, rend - r - ROWS), B, h);
       }
     }
     rho = seg_end;
@@ -800,26 +827,29 @@ __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, ui
 // order.  Unit = (token, 64 columns), one wave.
 __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int nd = (P.d + kWave - 1) / kWave;
+  constexpr int kCols = 2 * kWave;  // two columns (one 16-byte load of tagged words) per lane
+  const int nd = (P.d + kCols - 1) / kCols;
   const int nunits = P.T * nd;
   for (int u = gw; u < nunits; u += NW) {
-    const int t = u / nd, c = (u % nd) * kWave + lane;
+    const int t = u / nd, c = (u % nd) * kCols + 2 * lane;  // d is even: c < d means c + 1 < d
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.yq + (size_t)t * P.k * P.d, (uint32_t)(P.k * P.d) * 8u);
     const uint64_t t0 = wall_clock64();
+  int round = 0;
     for (;;) {
       bool ok = true;
-      float acc = 0.f;
-      if (c < P.d) {
-        for (int j = 0; j < P.k; ++j) {
-          const uint64_t wv = ld_tagged(&P.yq[((size_t)t * P.k + j) * P.d + c]);
-          ok &= tag_ok(wv, tag);
-          acc += tag_f32(wv);
-        }
+      float a0 = 0.f, a1 = 0.f;
+      const uint32_t cc = (uint32_t)min(c, P.d - 2);
+      for (int j = 0; j < P.k; ++j) {
+        const u32x4_t q = ld_coherent16(rs, ((uint32_t)j * P.d + cc) * 8u);
+        ok &= (q.y == tag) && (q.w == tag);
+        a0 += u2f(q.x);
+        a1 += u2f(q.z);
       }
       if (__all(ok)) {
-        if (c < P.d) P.out[(size_t)t * P.d + c] = acc;
+        if (c < P.d) *reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c) = make_float2(a0, a1);
         break;
       }
-      if (!keep_waiting(P, tag, t0)) return false;
+      if (!keep_waiting(P, tag, t0, kSiteY, u, round)) return false;
     }
   }
   return true;

@@ -43,7 +43,9 @@ def run_case(env, cfg, staged=False, check_inter=True, x=None, wr=None, p=None, 
     ws = moe.alloc_workspace(dims, cfg.k)
     out = moe.forward(xt, wrt, pt, st, cfg.k, workspace=ws, staged=staged, dims=dims)
     torch.cuda.synchronize()
-    assert moe.status(ws) == moe.MOE_OK
+    hdr = ws[:32].view(torch.int32).cpu().numpy()  # header words: status, abort, wait site, index
+    st = moe.status(ws)
+    assert st == moe.MOE_OK, f"status {st}, watchdog site {hdr[3]} index {hdr[4]}"
     got = out.cpu().numpy()
     it = {k: v.cpu().numpy() for k, v in moe.intermediates(ws, dims, cfg.k).items()}
     check_routing(it["topk_idx"], it["topk_w"], it["offsets"], it["sorted_slot"], ref, cfg.k)
@@ -52,9 +54,7 @@ def run_case(env, cfg, staged=False, check_inter=True, x=None, wr=None, p=None, 
     assert int(it["n_active"][0]) == n_act
     act = np.nonzero(np.diff(ref.offsets) > 0)[0]
     assert (it["active"][:n_act] == act).all()
-    err = rel_err(got, ref.out)
-    assert err <= OUT_TOL, f"output error {err}"
-    if check_inter:
+    if check_inter:  # intermediates first: a failure names the step
         for e in act:
             p0, p1 = ref.offsets[e], ref.offsets[e + 1]
             eh = rel_err(it["h"][p0:p1], ref.h[p0:p1])
@@ -65,6 +65,8 @@ def run_case(env, cfg, staged=False, check_inter=True, x=None, wr=None, p=None, 
             yref[slot] = ref.gates[t, j] * ref.y[ref.pos[slot]]
         ey = rel_err(it["y"], yref)
         assert ey <= INTER_TOL, f"y error {ey}"
+    err = rel_err(got, ref.out)
+    assert err <= OUT_TOL, f"output error {err}"
     print(f"[case] ok: out err {err:.2e}", flush=True)
     return got, ref, it
 
