@@ -62,7 +62,20 @@ def main():
     ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this layer runs on one GPU; multi-GPU sharding (expert or tensor parallel) "
