@@ -85,7 +85,7 @@ typedef enum {
 } moe_status;
 
 /* Layer sizes: T tokens, hidden size d, expert ffn size, E experts.  Limits:
- * T >= 0, d and ffn multiples of 32, 32 <= d <= 16384, 32 <= ffn <= 8192, 1 <= E <= 1024,
+ * T >= 0, d and ffn multiples of 32, 32 <= d <= 8192, 32 <= ffn <= 4096, 1 <= E <= 1024,
  * E * ceil(T / 64) <= 4096 (so T <= 1024 with 256 experts), 1 <= topk <= min(E, 64). */
 typedef struct {
   int32_t T;
@@ -155,6 +155,16 @@ typedef struct {
  * with MOE_ETIMEOUT. */
 #define MOE_OPT_WITHHOLD_ARRIVAL 0x1u
 
+/* Step trace: the first wave of every workgroup of the persistent launch
+ * writes the device wall clock (hipDeviceAttributeWallClockRate kHz) when it
+ * ends each step, into the workspace's trace region (offset `trace` of
+ * moe_mxfp4_ws_layout): uint64 [grid][16], slots 0 start, 1 router (and x
+ * staged), 7 own top-k tokens published, 2 all top-k results read,
+ * 3 permutation, 4 gate/up, 8 first h needed by the down step present,
+ * 5 down, 6 combine; 9-15 the gate/up end of waves 1-7 (slot 4 is wave 0's).
+ * Costs one store per step and workgroup. */
+#define MOE_OPT_TRACE 0x2u
+
 /* moe_mxfp4_forward with options (opts may be NULL). */
 int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
                          const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
@@ -181,9 +191,9 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
  * 32 bits are the fp32 value (the high 32 bits are a tag); logits fp32 [T][E];
  * topk_idx int32 [T][topk]; topk_w fp32 [T][topk]; offsets int32 [E+1];
  * sorted_slot, pos int32 [T*topk]; active int32 [E] (experts with at least one
- * token, ascending); n_active int32. */
+ * token, ascending); n_active int32; trace: see MOE_OPT_TRACE. */
 typedef struct {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, total;
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, trace, total;
 } moe_mxfp4_ws_layout;
 int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxfp4_ws_layout* layout);
 

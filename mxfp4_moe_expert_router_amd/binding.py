@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ETIMEOUT, MOE_EDEVICE, MOE_EALIGN = range(8)
 MOE_OPT_WITHHOLD_ARRIVAL = 0x1
+MOE_OPT_TRACE = 0x2
 
 
 class MoeError(RuntimeError):
@@ -37,7 +38,7 @@ class Options(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("logits", "topk_idx", "topk_w", "offsets", "sorted_slot", "pos", "active", "n_active", "h", "y",
+                ("logits", "topk_idx", "topk_w", "offsets", "sorted_slot", "pos", "active", "n_active", "h", "y", "trace",
                  "total")]
 
 
@@ -247,4 +248,5 @@ def intermediates(workspace: torch.Tensor, dims: LayerDims, topk: int) -> dict:
         "n_active": view(lay.n_active, 1, torch.int32),
         "h": tagged(lay.h, TK * F).view(TK, F),
         "y": tagged(lay.y, TK * d).view(TK, d),
+        "trace": view(lay.trace, 2048 * 16, torch.int64).view(2048, 16),
     }

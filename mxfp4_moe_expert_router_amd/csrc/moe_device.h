@@ -102,27 +102,72 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
-// Row-level steps use DPP (xor 1, xor 2, half-row mirror, row mirror), the
-// cross-row steps use bpermute shuffles.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// gfx950 lane swaps across rows.  With the same register as both operands,
+// permlane16_swap returns {row 2n, row 2n+1} and permlane32_swap returns
+// {lanes 0-31, lanes 32-63}, each in both lanes of a pair: element 0 holds
+// the lower lane's value, element 1 the upper lane's (partner = lane ^ 16,
+// lane ^ 32).  No LDS round trip, unlike a bpermute shuffle.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the same total (the
+// operands of each step are added in lane order, so all lanes agree bit for
+// bit).  Row steps: DPP xor 1, xor 2, half-row mirror, row mirror; then the
+// two cross-row swaps.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
   v += dpp_f<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  uint32_t a, b;
+  swap16(__builtin_bit_cast(uint32_t, v), a, b);
+  v = u2f(a) + u2f(b);
+  swap32(__builtin_bit_cast(uint32_t, v), a, b);
+  return u2f(a) + u2f(b);
+}
+
+// Maximum of a 64-bit key over the 64 lanes; every lane receives it.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t k) {
+  const uint64_t o = ((uint64_t)dpp_u<CTRL>((uint32_t)(k >> 32)) << 32) | dpp_u<CTRL>((uint32_t)k);
+  return max_u64(k, o);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_u64<0xB1>(k);
+  k = dpp_max_u64<0x4E>(k);
+  k = dpp_max_u64<0x141>(k);
+  k = dpp_max_u64<0x140>(k);
+  uint32_t hl, hh, ll, lh;
+  swap16((uint32_t)(k >> 32), hl, hh);
+  swap16((uint32_t)k, ll, lh);
+  k = max_u64(((uint64_t)hl << 32) | ll, ((uint64_t)hh << 32) | lh);
+  swap32((uint32_t)(k >> 32), hl, hh);
+  swap32((uint32_t)k, ll, lh);
+  return max_u64(((uint64_t)hl << 32) | ll, ((uint64_t)hh << 32) | lh);
 }
 
 // Eight per-lane partial sums v[0..7] -> every lane receives the wave-wide
 // total of value (lane >> 3).  Reduce-scatter: exchange half of the values
 // across lane bits 5, 4 and 3, then sum the remaining value over lane bits
-// 0..2.  Costs ~30 VALU ops and 6 shuffles instead of 8 full reductions.
+// 0..2.  Costs ~30 VALU ops and 6 lane swaps instead of 8 full reductions.
 __device__ __forceinline__ float reduce8(const float v[8]) {
   const int lane = threadIdx.x & (kWave - 1);
   const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
@@ -131,14 +176,18 @@ __device__ __forceinline__ float reduce8(const float v[8]) {
   for (int i = 0; i < 4; ++i) {
     const float keep = b5 ? v[i + 4] : v[i];
     const float send = b5 ? v[i] : v[i + 4];
-    w[i] = keep + __shfl_xor(send, 32, kWave);
+    uint32_t lo, hi;
+    swap32(__builtin_bit_cast(uint32_t, send), lo, hi);
+    w[i] = keep + u2f(b5 ? lo : hi);  // the partner lane's `send`
   }
   float x[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float keep = b4 ? w[i + 2] : w[i];
     const float send = b4 ? w[i] : w[i + 2];
-    x[i] = keep + __shfl_xor(send, 16, kWave);
+    uint32_t lo, hi;
+    swap16(__builtin_bit_cast(uint32_t, send), lo, hi);
+    x[i] = keep + u2f(b4 ? lo : hi);
   }
   float y;
   {

@@ -29,9 +29,9 @@
 // words produced by earlier steps of (possibly other) co-resident workgroups.
 //
 // Steps:
-//   router   units (expert, half of d, 8 tokens), one wave each -> tagged partial logits
-//   top-k    small batches: every workgroup redundantly, from the tagged logits;
-//            large batches: one wave per token -> tagged expert ids and gates
+//   router   units (expert, 8 tokens), one workgroup each, its waves splitting d
+//            -> tagged logits
+//   top-k    one wave per token -> tagged {expert id, gate} records, 8 copies
 //   permute  every workgroup builds the (expert, token) permutation in LDS
 //   gate/up  small batches: all of x resident in LDS, each wave streams a
 //            contiguous range of (expert, row) pairs of W_gate/W_up;
@@ -63,9 +63,8 @@ namespace moe {
 constexpr int kWG = 512;               // threads per workgroup
 constexpr int kWaves = kWG / kWave;    // waves per workgroup
 constexpr int kLdsMax = 160 * 1024 - 1024;  // dynamic LDS per workgroup (gfx950 has 160 KiB; static LDS needs a few bytes)
-constexpr int kRouterParts = 2;        // a router unit covers d / kRouterParts columns
 constexpr int kRouterTok = 8;          // tokens per router unit
-constexpr int kRouterF4 = 16;          // float4 per lane per router unit (d <= 8192)
+constexpr int kRouterF4 = 4;           // float4 per lane of a router unit's wave (d / 8 <= 1024 columns)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxD = 8192;
@@ -76,6 +75,8 @@ constexpr int kMaxTokLds = 8;          // token rows per x staging pass (large b
 constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
 constexpr int kMaxGrid = 2048;
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
+constexpr int kTraceSlots = 16;        // wall-clock stamps per workgroup (trace option)
+constexpr int kTopkRep = 8;            // copies of the top-k results (each read by 1/8 of the grid)
 
 // Header words (first kHdrBytes of the workspace).
 enum { kEpoch = 0, kStatus = 1, kAbort = 2, kWhere = 3, kWhat = 4, kStarted = 64 };
@@ -89,9 +90,8 @@ struct Params {
   const uint8_t* scales;
   float* out;
   uint32_t* hdr;
-  uint64_t* lgp;   // [T][E][kRouterParts] tagged partial logits
-  uint64_t* tki;   // [T*k] tagged expert ids   (large batches)
-  uint64_t* tkw;   // [T*k] tagged gates        (large batches)
+  uint64_t* lgp;   // [T][E rounded up to even] tagged logits
+  uint64_t* tk;    // [kTopkRep][T*k][2] tagged {expert id, gate} per slot, replicated
   uint64_t* hq;    // [T*k][F] tagged h, pair order
   uint64_t* yq;    // [T*k][d] tagged gate * y, slot order
   float* logits;   // plain copies for inspection
@@ -102,6 +102,7 @@ struct Params {
   int32_t* pos;
   int32_t* active;
   int32_t* n_active;
+  uint64_t* trace;    // [grid][kTraceSlots] wall-clock stamps, or null
   uint64_t spin_ticks;
   uint32_t withhold;  // test knob: top-k waits for a tag the router never writes
   int ntl;            // tokens per x staging pass (large batches)
@@ -110,7 +111,7 @@ struct Params {
 // ------------------------------------------------------------ LDS layout ----
 // Shared by host (size) and device (carving).
 struct LdsPlan {
-  size_t xs, mask, tki, tkw, off, slot, act, misc, total;
+  size_t xs, mask, tki, tkw, off, slot, act, cgu, cdn, misc, total;
 };
 
 __host__ __device__ inline size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -136,6 +137,8 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool sma
   L.off = o; o = al16(o + ((size_t)E + 1) * 4);
   L.slot = o; o = al16(o + TK * 4);
   L.act = o; o = al16(o + (size_t)E * 4);
+  L.cgu = o; o = al16(o + ((size_t)E + 1) * 4);
+  L.cdn = o; o = al16(o + ((size_t)E + 1) * 4);
   L.misc = o; o = al16(o + 64 * 4);
   L.total = o;
   return L;
@@ -149,6 +152,8 @@ struct Smem {
   int* off;
   int* slot;
   int* act;
+  int* cgu;   // [n_active + 1] cumulative gate/up work per row, over active experts
+  int* cdn;   // [n_active + 1] same for down
   int* misc;  // [0] n_active, [8..8+kWaves) scan scratch
 };
 
@@ -163,6 +168,8 @@ __device__ __forceinline__ Smem carve(char* base, const Params& P, bool small, i
   S.off = reinterpret_cast<int*>(base + L.off);
   S.slot = reinterpret_cast<int*>(base + L.slot);
   S.act = reinterpret_cast<int*>(base + L.act);
+  S.cgu = reinterpret_cast<int*>(base + L.cgu);
+  S.cdn = reinterpret_cast<int*>(base + L.cdn);
   S.misc = reinterpret_cast<int*>(base + L.misc);
   return S;
 }
@@ -184,20 +191,21 @@ __device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag, uin
 }
 
 // One spin round of a wave-level wait: true to retry, false to give up.
-// Rounds back off exponentially (about 0.5 us doubling to 8 us) so that waves
-// that wait do not flood the memory system that the waves they wait for are
-// using.  The compiler memory barrier makes the caller's polling loads (plain
-// buffer loads, not atomics) be issued again on the next round instead of
-// being reused from registers.
+// Rounds back off exponentially from about 0.2 us up to 2^max_shift times
+// that, so that waiting waves do not flood the memory system that the waves
+// they wait for are using, without oversleeping much past the arrival.  The
+// compiler memory barrier makes the caller's polling loads (plain buffer
+// loads, not atomics) be issued again on the next round instead of being
+// reused from registers.
 __device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint64_t t0, uint32_t site,
-                                             uint32_t what, int& round) {
+                                             uint32_t what, int& round, int max_shift) {
   if (aborted(P, tag)) return false;
   if (wall_clock64() - t0 > P.spin_ticks) {
     raise_timeout(P, tag, site, what);
     return false;
   }
-  const int units = 1 << min(round, 4);
-  for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(20);
+  const int units = 1 << min(round, max_shift);
+  for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(8);
   ++round;
   __asm__ __volatile__("" ::: "memory");
   return true;
@@ -239,132 +247,161 @@ __device__ __forceinline__ void end_call(const Params& P, uint32_t tag, int G) {
   }
 }
 
+// Trace option: the first wave of workgroup `wg` stamps the end of step `i`.
+__device__ __forceinline__ void stamp(const Params& P, int wg, int i) {
+  if (P.trace != nullptr && threadIdx.x == 0) P.trace[(size_t)wg * kTraceSlots + i] = wall_clock64();
+}
+// Trace option: waves 1..7 of workgroup `wg` stamp the end of their gate/up rows.
+__device__ __forceinline__ void stamp_gu_wave(const Params& P, int wg) {
+  const int wave = threadIdx.x / kWave;
+  if (P.trace != nullptr && wave > 0 && (threadIdx.x & (kWave - 1)) == 0)
+    P.trace[(size_t)wg * kTraceSlots + 8 + wave] = wall_clock64();
+}
+
 // ---------------------------------------------------------------- router ----
 // logits[t][e] = sum_c x[t][c] * W_r[e][c] in fp32 ([P1-FP4]/[P3-FP4]: the
-// router stays at higher precision than the experts).  Unit = (expert, part
-// of d, group of 8 tokens), one wave; the two partial sums of a logit are
-// added in a fixed order by the consumer.
-__device__ __forceinline__ void router_step(const Params& P, uint32_t tag, int gw, int NW) {
-  const int lane = threadIdx.x & (kWave - 1);
+// router stays at higher precision than the experts).  Unit = (expert, group
+// of 8 tokens), one workgroup: wave v covers columns [v*d/8, (v+1)*d/8) of
+// the expert's row held in registers, the 8 per-wave partial sums of a logit
+// are added in wave order.  XLDS: x comes from the LDS copy (piece-transposed,
+// see stage_x), else from global memory.  `pre` (all threads) runs once, after
+// the first unit's weight loads are issued: it overlaps the x staging with
+// them.  All threads of the workgroup.
+template <bool XLDS, class Pre>
+__device__ __forceinline__ void router_step(const Params& P, const Smem& S, uint32_t tag, int wg, int G, Pre pre) {
+  __shared__ float s_part[kWaves][kRouterTok];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int ngr = (P.T + kRouterTok - 1) / kRouterTok;
-  const int nunits = P.E * kRouterParts * ngr;
-  const int dp = P.d / kRouterParts;
-  const int n4 = dp / 4;
-  for (int u = gw; u < nunits; u += NW) {
-    const int g = u % ngr;
-    const int part = (u / ngr) % kRouterParts;
-    const int e = u / (ngr * kRouterParts);
+  const int nunits = P.E * ngr;
+  const int dw = P.d / kWaves;  // a multiple of 4 (d is a multiple of 32)
+  const int n4 = dw / 4;        // <= kRouterF4 * kWave
+  const int NCH = P.d / 32;
+  const int E2 = (P.E + 1) & ~1;
+  bool first = true;
+  for (int u = wg; u < nunits; u += G) {
+    const int e = u / ngr, g = u % ngr;
     const int t0 = g * kRouterTok, nt = min(kRouterTok, P.T - t0);
-    const int c0 = part * dp;
+    const int c0 = wave * dw;
     const f32x4_t* w = reinterpret_cast<const f32x4_t*>(P.wr + (size_t)e * P.d + c0);
     f32x4_t wv[kRouterF4];
 #pragma unroll
     for (int i = 0; i < kRouterF4; ++i) {
-      if (kWave * i < n4) {  // uniform; the tail lanes read a valid chunk and get a zero weight
-        const int c = lane + kWave * i;
-        const f32x4_t v = w[min(c, n4 - 1)];
-        wv[i] = c < n4 ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      const int c = lane + kWave * i;
+      const f32x4_t v = w[min(c, n4 - 1)];  // tail lanes re-read a valid chunk and get a zero weight
+      wv[i] = c < n4 ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (first) {
+      pre();
+      first = false;
     }
     float acc[kRouterTok];
 #pragma unroll
     for (int j = 0; j < kRouterTok; ++j) {
       acc[j] = 0.f;
-      if (j < nt) {
-        const uint16_t* xt = P.x + (size_t)(t0 + j) * P.d + c0;
+      if (j < nt) {  // uniform
 #pragma unroll
         for (int i = 0; i < kRouterF4; ++i) {
-          if (kWave * i < n4) {
-            const int c = min(lane + kWave * i, n4 - 1);
-            const uint2 xv = *reinterpret_cast<const uint2*>(xt + (size_t)c * 4);
-            acc[j] = fmaf(wv[i].x, bf16lo(xv.x), acc[j]);
-            acc[j] = fmaf(wv[i].y, bf16hi(xv.x), acc[j]);
-            acc[j] = fmaf(wv[i].z, bf16lo(xv.y), acc[j]);
-            acc[j] = fmaf(wv[i].w, bf16hi(xv.y), acc[j]);
+          const int col = c0 + 4 * min(lane + kWave * i, n4 - 1);
+          uint2 xv;
+          if (XLDS) {
+            const int ch = col / 32, q = (col % 32) / 8, half = (col % 8) / 4;
+            xv = reinterpret_cast<const uint2*>(S.xs)[((size_t)(t0 + j) * 4 * NCH + q * NCH + ch) * 2 + half];
+          } else {
+            xv = *reinterpret_cast<const uint2*>(P.x + (size_t)(t0 + j) * P.d + col);
           }
+          acc[j] = fmaf(wv[i].x, bf16lo(xv.x), acc[j]);
+          acc[j] = fmaf(wv[i].y, bf16hi(xv.x), acc[j]);
+          acc[j] = fmaf(wv[i].z, bf16lo(xv.y), acc[j]);
+          acc[j] = fmaf(wv[i].w, bf16hi(xv.y), acc[j]);
         }
       }
     }
+    const float s = reduce8(acc);  // lanes 8j..8j+7: token j's sum over this wave's columns
+    if ((lane & 7) == 0) s_part[wave][lane >> 3] = s;
+    __syncthreads();
+    if (wave == 0 && lane < nt) {
+      float l = 0.f;
 #pragma unroll
-    for (int j = 0; j < kRouterTok; ++j) {
-      const float s = wave_sum(acc[j]);
-      if (lane == j && j < nt)
-        st_tagged(&P.lgp[((size_t)(t0 + j) * P.E + e) * kRouterParts + part], __builtin_bit_cast(uint32_t, s), tag);
+      for (int v = 0; v < kWaves; ++v) l += s_part[v][lane];
+      st_tagged(&P.lgp[(size_t)(t0 + lane) * E2 + e], __builtin_bit_cast(uint32_t, l), tag);
     }
+    __syncthreads();
   }
+  if (first) pre();
 }
 
 // ---------------------------------------------------------------- top-k -----
 // One wave, token t: gathers the tagged logits, selects the k largest in
 // (logit desc, expert asc) order and their softmax over the selected set
 // ([P3-FP4] top-k routing).  Lane j < k returns expert j and gate j.
-// Returns false if the wait was abandoned.
+// Returns false if the wait was abandoned.  Lane L holds the logits of
+// experts 2(L + 64m) + b in v[2m + b] (one 16-byte load per pair).
 __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t, int* out_i, float* out_w, bool debug) {
   constexpr int VPL = kMaxE / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t want = tag + P.withhold;
+  const int E2 = (P.E + 1) & ~1, np = E2 / 2;
   float v[VPL];
-  static_assert(kRouterParts == 2, "one 16-byte load holds the two partial logits of an expert");
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.lgp + (size_t)t * P.E * kRouterParts, P.E * kRouterParts * 8);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.lgp + (size_t)t * E2, (uint32_t)E2 * 8u);
   const uint64_t t0 = wall_clock64();
   int round = 0;
   for (;;) {
     bool ok = true;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      v[i] = 0.f;
-      if (kWave * i < P.E) {  // uniform
-        const int e = lane + kWave * i;
-        const u32x4_t q = ld_coherent16(rs, (uint32_t)min(e, P.E - 1) * 16u);
-        if (e < P.E) {
-          ok &= (q.y == want) && (q.w == want);
-          v[i] = u2f(q.x) + u2f(q.z);
+    for (int m = 0; m < VPL / 2; ++m) {
+      v[2 * m] = v[2 * m + 1] = 0.f;
+      if (kWave * m < np) {  // uniform
+        const int p = lane + kWave * m;
+        const u32x4_t q = ld_coherent16(rs, (uint32_t)min(p, np - 1) * 16u);
+        if (2 * p < P.E) {
+          ok &= q.y == want;
+          v[2 * m] = u2f(q.x);
+        }
+        if (2 * p + 1 < P.E) {
+          ok &= q.w == want;
+          v[2 * m + 1] = u2f(q.z);
         }
       }
     }
     if (__all(ok)) break;
-    if (!keep_waiting(P, tag, t0, kSiteLogits, t, round)) return false;
+    if (!keep_waiting(P, tag, t0, kSiteLogits, t, round, 2)) return false;
   }
   if (debug) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
+      const int e = 2 * (lane + kWave * (i / 2)) + (i & 1);
       if (e < P.E) P.logits[(size_t)t * P.E + e] = v[i];
     }
   }
-  uint32_t taken = 0;
-  float my_v = 0.f, vmax = 0.f;
-  int my_i = 0;
-  for (int j = 0; j < P.k; ++j) {
-    float bv = 0.f;
-    int bi = 0x7FFFFFFF;
+  // (logit desc, expert asc) as one 64-bit key: order-preserving logit bits
+  // (-0 taken as +0) above the complemented expert index; 0 = no candidate.
+  uint64_t key[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < P.E && !((taken >> i) & 1u)) {
-        if (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi)) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      const bool better = (bi == 0x7FFFFFFF) || (oi != 0x7FFFFFFF && (ov > bv || (ov == bv && oi < bi)));
-      if (better) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (j == 0) vmax = bv;
-    if (lane == j) {
-      my_v = bv;
-      my_i = bi;
-    }
+  for (int i = 0; i < VPL; ++i) {
+    const int e = 2 * (lane + kWave * (i / 2)) + (i & 1);
+    const uint32_t b = __builtin_bit_cast(uint32_t, v[i] + 0.f);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    key[i] = e < P.E ? ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e : 0ull;
   }
+  uint64_t mine = 0, top = 0;
+  for (int j = 0; j < P.k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (kWave * (i / 2) < np) best = max_u64(best, key[i]);  // uniform guard
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (key[i] == best) key[i] = 0ull;  // keys are distinct: one lane drops it
+    if (j == 0) top = best;
+    if (lane == j) mine = best;
+  }
+  auto key_value = [](uint64_t kk) {
+    const uint32_t o = (uint32_t)(kk >> 32);
+    return u2f((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+  };
+  const float my_v = key_value(mine), vmax = key_value(top);
+  const int my_i = (int)~(uint32_t)mine;
   const float ex = (lane < P.k) ? expf(my_v - vmax) : 0.f;
   const float z = wave_sum(ex);
   *out_i = my_i;
@@ -372,40 +409,40 @@ __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t,
   return true;
 }
 
-// Every workgroup computes all tokens' top-k into LDS (small batches).
-__device__ __forceinline__ bool topk_local(const Params& P, const Smem& S, uint32_t tag, bool debug) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  bool ok = true;
-  for (int t = wave; t < P.T && ok; t += kWaves) {
-    int ii;
-    float ww;
-    ok = topk_token(P, tag, t, &ii, &ww, debug);
-    if (ok && lane < P.k) {
-      S.tki[t * P.k + lane] = ii;
-      S.tkw[t * P.k + lane] = ww;
-    }
-  }
-  return ok;
-}
-
-// One wave per token across the grid; results as tagged words (large batches).
-__device__ __forceinline__ bool topk_global(const Params& P, uint32_t tag, int gw, int NW) {
+// Token t's top-k is computed by one wave (the owner) and published as
+// tagged records in kTopkRep copies; every workgroup then reads the copy
+// wg % kTopkRep.  Publishing 16 bytes per slot instead of having every
+// workgroup gather all T*E logits keeps the many-reader traffic off the few
+// memory channels that hold the logits.  Owners: for T <= NW, waves
+// t * NW / T (spread over the grid), else waves t mod NW.
+__device__ __forceinline__ bool topk_publish(const Params& P, uint32_t tag, int gw, int NW) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int t = gw; t < P.T; t += NW) {
+  const int T = P.T, TK = P.T * P.k;
+  int t = T <= NW ? (int)(((int64_t)gw * T + NW - 1) / NW) : gw;
+  if (T <= NW && (t >= T || (int)((int64_t)t * NW / T) != gw)) return true;
+  for (; t < T; t += NW) {
     int ii;
     float ww;
     if (!topk_token(P, tag, t, &ii, &ww, true)) return false;
     if (lane < P.k) {
-      st_tagged(&P.tki[(size_t)t * P.k + lane], (uint32_t)ii, tag);
-      st_tagged(&P.tkw[(size_t)t * P.k + lane], __builtin_bit_cast(uint32_t, ww), tag);
+      const uint32_t wb = __builtin_bit_cast(uint32_t, ww);
+#pragma unroll
+      for (int r = 0; r < kTopkRep; ++r) {
+        uint64_t* rec = P.tk + ((size_t)r * TK + (size_t)t * P.k + lane) * 2;
+        st_tagged(rec, (uint32_t)ii, tag);
+        st_tagged(rec + 1, wb, tag);
+      }
     }
+    if (T <= NW) break;
   }
   return true;
 }
 
-// Copy all tagged top-k results into LDS (waits for them).  All threads.
-__device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32_t tag) {
+// Copy all top-k records of copy `rep` into LDS (waits for them).  All
+// threads; each wave polls only its own slots.
+__device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32_t tag, int rep) {
   const int TK = P.T * P.k;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.tk + (size_t)rep * TK * 2, (uint32_t)TK * 16u);
   bool ok = true;
   const uint64_t t0 = wall_clock64();
   int round = 0;
@@ -414,15 +451,15 @@ __device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32
     for (;;) {
       bool ready = true;
       if (s < TK) {
-        const uint64_t a = ld_tagged(&P.tki[s]), b = ld_tagged(&P.tkw[s]);
-        ready = tag_ok(a, tag) && tag_ok(b, tag);
+        const u32x4_t q = ld_coherent16(rs, (uint32_t)s * 16u);
+        ready = q.y == tag && q.w == tag;
         if (ready) {
-          S.tki[s] = tag_i32(a);
-          S.tkw[s] = tag_f32(b);
+          S.tki[s] = (int)q.x;
+          S.tkw[s] = u2f(q.z);
         }
       }
       if (__all(ready)) break;
-      if (!keep_waiting(P, tag, t0, kSiteTopk, base, round)) {
+      if (!keep_waiting(P, tag, t0, kSiteTopk, base, round, 2)) {
         ok = false;
         break;
       }
@@ -450,6 +487,39 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   __syncthreads();
   *total = tot;
   return base + inc - v;
+}
+
+// Work model of the expert steps, per row of an expert with n tokens (from
+// per-wave timings on MI355X): a gate/up row pair costs 16 + 3 per extra
+// token (the weights are read once, the decode and dot products repeat);
+// a W_down row costs 10 per pass over the row plus 4 for the second token of
+// a two-token pass (F <= 2048 takes tokens two at a time).
+__device__ __forceinline__ int gu_cost(int n) { return 16 + 3 * (n - 1); }
+__device__ __forceinline__ int dn_cost(int n, int F) { return F <= 2048 ? 14 * (n / 2) + 10 * (n % 2) : 10 * n; }
+
+// Index, in the (active expert, row) list with R rows per expert, of the
+// first row whose modelled start lies at or after work position c (c in
+// [0, R * cum[na]]).  cum: cumulative work per row of the active experts.
+__device__ __forceinline__ int row_at(const int* cum, int na, int R, int64_t c) {
+  const int cq = (int)(c / R);
+  int lo = 0, hi = na;  // largest a with cum[a] <= cq
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uni(cum[mid]) <= cq) lo = mid;
+    else hi = mid - 1;
+  }
+  if (lo >= na) return na * R;
+  const int u = uni(cum[lo + 1]) - uni(cum[lo]);
+  const int64_t rem = c - (int64_t)R * uni(cum[lo]);
+  const int i = (int)((rem + u - 1) / u);
+  return lo * R + min(i, R);
+}
+
+// Rows [q0, q1) of wave gw of NW: equal shares of the modelled work.
+__device__ __forceinline__ void work_range(const int* cum, int na, int R, int gw, int NW, int& q0, int& q1) {
+  const int64_t C = (int64_t)R * uni(cum[na]);
+  q0 = row_at(cum, na, R, C * gw / NW);
+  q1 = row_at(cum, na, R, C * (gw + 1) / NW);
 }
 
 // All threads of the workgroup.  Reads S.tki / S.tkw, writes S.off / S.slot /
@@ -507,6 +577,37 @@ __device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool 
     }
   }
   __syncthreads();
+  {
+    // cumulative modelled work of the active experts (see gu_cost, dn_cost)
+    const int na = S.misc[0];
+    int g2[2], d2[2], gs = 0, ds = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int a = e0 + i;
+      const int n = a < na ? S.off[S.act[a] + 1] - S.off[S.act[a]] : 0;
+      g2[i] = a < na ? gu_cost(n) : 0;
+      d2[i] = a < na ? dn_cost(n, P.F) : 0;
+      gs += g2[i];
+      ds += d2[i];
+    }
+    int gt, dt;
+    int gb = block_exclusive_scan(gs, S.misc + 8, &gt);
+    int db = block_exclusive_scan(ds, S.misc + 8, &dt);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int a = e0 + i;
+      if (a < na) {
+        S.cgu[a] = gb;
+        S.cdn[a] = db;
+      }
+      gb += g2[i];
+      db += d2[i];
+    }
+    if (tid == 0) {
+      S.cgu[na] = gt;
+      S.cdn[na] = dt;
+    }
+  }
   for (int s = tid; s < TK; s += kWG) {
     const int t = s / P.k, e = S.tki[s];
     const uint64_t* me = mask + (size_t)e * W;
@@ -626,19 +727,38 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
   }
 }
 
-// Each wave streams a contiguous range of the n_active*F row pairs, loading
-// the next row pair while computing the current one.
-__device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
-  const int64_t total = (int64_t)S.misc[0] * P.F;
-  const int q0 = (int)(total * gw / NW), q1 = (int)(total * (gw + 1) / NW);
-  if (q0 >= q1) return;
+// Next unit from a workgroup's LDS work counter (one LDS atomic by lane 0).
+__device__ __forceinline__ int grab(int* ctr) {
+  int v = 0;
+  if ((threadIdx.x & (kWave - 1)) == 0) v = atomicAdd(ctr, 1);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Each workgroup owns a contiguous range of the n_active*F row pairs (equal
+// shares of the modelled work per workgroup); its waves take the row pairs one
+// at a time from an LDS counter (S.misc[1], set by set_counters), so the two
+// waves that share a SIMD, which issue at different rates, finish together.
+// A wave loads its next row pair while computing the current one.
+__device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  int Q0, Q1;
+  work_range(S.cgu, uni(S.misc[0]), P.F, wg, G, Q0, Q1);
+  int* ctr = S.misc + 1;
+  int r0 = grab(ctr);
+  if (r0 >= Q1) return;
   GURow A, B;
-  gu_load(P, S, q0, A);
-  for (int rho = q0; rho < q1; rho += 2) {
-    gu_load(P, S, min(rho + 1, q1 - 1), B);  // the last odd step re-reads a row it does not use
-    gu_compute_resident(P, S, tag, rho, A);
-    gu_load(P, S, min(rho + 2, q1 - 1), A);
-    if (rho + 1 < q1) gu_compute_resident(P, S, tag, rho + 1, B);
+  gu_load(P, S, r0, A);
+  for (;;) {
+    // past the end of the range a wave re-reads the row pair it just loaded
+    // (cache-hot) and does not use it
+    const int r1 = grab(ctr);
+    gu_load(P, S, r1 < Q1 ? r1 : r0, B);
+    gu_compute_resident(P, S, tag, r0, A);
+    if (r1 >= Q1) break;
+    const int r2 = grab(ctr);
+    gu_load(P, S, r2 < Q1 ? r2 : r1, A);
+    gu_compute_resident(P, S, tag, r1, B);
+    if (r2 >= Q1) break;
+    r0 = r2;
   }
 }
 
@@ -736,7 +856,7 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
       }
       if (__all(ok)) return true;
     }
-    if (!keep_waiting(P, tag, t0, kSiteH, p, round)) return false;
+    if (!keep_waiting(P, tag, t0, kSiteH, p, round, 3)) return false;
   }
 }
 
@@ -776,50 +896,131 @@ __device__ __forceinline__ void dn_compute(const Params& P, const Smem& S, uint3
   }
 }
 
-// Each wave streams a contiguous range of the n_active*d rows of W_down,
-// ROWS rows per step with the next step's rows in flight.
+// Rows [r, rend) of expert e's W_down against the h of NT-or-fewer pairs
+// starting at pair p (ntok of them), ROWS rows per step with the next step's
+// rows in flight.
 template <int MM, int NT, int ROWS>
-__device__ __forceinline__ bool down_waves(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
+__device__ __forceinline__ bool down_rows(const Params& P, const Smem& S, uint32_t tag, int e, int p, int ntok, int r,
+                                          int rend) {
+  float h[NT][MM][32];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    if (tt < ntok) {
+      if (!dn_load_h<MM>(P, tag, p + tt, h[tt])) return false;
+    }
+  }
+  DnRows<MM, ROWS> A, B;
+  dn_load<MM, ROWS>(P, e, r, min(ROWS, rend - r), A);
+  for (; r < rend; r += 2 * ROWS) {
+    // prefetches past the segment end re-read its last row and are not used
+    const int rB = min(r + ROWS, rend - 1), rA2 = min(r + 2 * ROWS, rend - 1);
+    dn_load<MM, ROWS>(P, e, rB, min(ROWS, rend - rB), B);
+    dn_compute<MM, NT, ROWS>(P, S, tag, p, ntok, r, min(ROWS, rend - r), A, h);
+    dn_load<MM, ROWS>(P, e, rA2, min(ROWS, rend - rA2), A);
+    if (r + ROWS < rend) dn_compute<MM, NT, ROWS>(P, S, tag, p, ntok, r + ROWS, min(ROWS, rend - r - ROWS), B, h);
+  }
+  return true;
+}
+
+// F > 2048: each wave streams a contiguous range of the n_active*d rows of
+// W_down (equal shares of the modelled work), one token per pass.
+template <int MM>
+__device__ __forceinline__ bool down_waves_static(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
   const int d = P.d;
-  const int64_t total = (int64_t)S.misc[0] * d;
-  const int q0 = (int)(total * gw / NW), q1 = (int)(total * (gw + 1) / NW);
+  int q0, q1;
+  work_range(S.cdn, uni(S.misc[0]), d, gw, NW, q0, q1);
   int rho = q0;
   while (rho < q1) {
     const int a = uni(rho / d);
     const int seg_end = min(q1, (a + 1) * d);
     const int e = uni(S.act[a]);
     const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
-    for (int tg = 0; tg < ne; tg += NT) {
-      const int ntok = min(NT, ne - tg);
-      float h[NT][MM][32];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        if (tt < ntok) {
-          if (!dn_load_h<MM>(P, tag, p0 + tg + tt, h[tt])) return false;
-        }
-      }
-      int r = rho - a * d;
-      const int rend = seg_end - a * d;
-      DnRows<MM, ROWS> A, B;
-      dn_load<MM, ROWS>(P, e, r, min(ROWS, rend - r), A);
-      for (; r < rend; r += 2 * ROWS) {
-        // prefetches past the segment end re-read its last row and are not used
-        const int rB = min(r + ROWS, rend - 1), rA2 = min(r + 2 * ROWS, rend - 1);
-        dn_load<MM, ROWS>(P, e, rB, min(ROWS, rend - rB), B);
-        dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, r, min(ROWS, rend - r), A, h);
-        dn_load<MM, ROWS>(P, e, rA2, min(ROWS, rend - rA2), A);
-        if (r + ROWS < rend) dn_compute<MM, NT, ROWS>(P, S, tag, p0 + tg, ntok, r + ROWS, min(ROWS, rend - r - ROWS), B, h);
-      }
-    }
+    const int r0 = rho - a * d, rend = seg_end - a * d;
+    for (int tg = 0; tg < ne; ++tg)
+      if (!down_rows<MM, 1, 2>(P, S, tag, e, p0 + tg, 1, r0, rend)) return false;
     rho = seg_end;
   }
   return true;
 }
 
+// Unit u of the down step: kDnRows consecutive rows of one active expert
+// (d / kDnRows units per expert).
+__device__ __forceinline__ void dn_unit_rows(const Params& P, const Smem& S, int u, DnRows<1, kDnRows>& R) {
+  const int upe = P.d / kDnRows;
+  const int a = uni(u / upe);
+  dn_load<1, kDnRows>(P, uni(S.act[a]), (u - a * upe) * kDnRows, kDnRows, R);
+}
+
+// One unit against every token of its expert, two tokens per pass; the h of
+// the pass is kept in registers across units of the same expert.
+__device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uint32_t tag, int u,
+                                             const DnRows<1, kDnRows>& R, float (&h)[2][1][32], int& ha, int& hb) {
+  const int upe = P.d / kDnRows;
+  const int a = uni(u / upe), e = uni(S.act[a]);
+  const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
+  const int r = (u - a * upe) * kDnRows;
+  for (int tg = 0; tg < ne; tg += 2) {
+    const int nt = min(2, ne - tg);
+    if (ha != a || hb != tg) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        if (tt < nt && !dn_load_h<1>(P, tag, p0 + tg + tt, h[tt])) return false;
+      if (ha < 0) stamp(P, blockIdx.x, 8);  // trace: the first h this wave needs is present
+      ha = a;
+      hb = tg;
+    }
+    dn_compute<1, 2, kDnRows>(P, S, tag, p0 + tg, nt, r, kDnRows, R, h);
+  }
+  return true;
+}
+
+// F <= 2048: each workgroup owns a contiguous range of the down units (equal
+// shares of the modelled work per workgroup); its waves take units from an
+// LDS counter (S.misc[2]) and load the next unit's rows while computing the
+// current one.  An expert's tokens are taken two at a time, so W_down is read
+// once per two tokens.
+__device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  int U0, U1;
+  work_range(S.cdn, uni(S.misc[0]), P.d / kDnRows, wg, G, U0, U1);
+  int* ctr = S.misc + 2;
+  float h[2][1][32];
+  int ha = -1, hb = -1;
+  int u0 = grab(ctr);
+  if (u0 >= U1) return true;
+  DnRows<1, kDnRows> A, B;
+  dn_unit_rows(P, S, u0, A);
+  for (;;) {
+    const int u1 = grab(ctr);
+    dn_unit_rows(P, S, u1 < U1 ? u1 : u0, B);  // past the end: re-read (cache-hot), unused
+    if (!dn_unit_work(P, S, tag, u0, A, h, ha, hb)) return false;
+    if (u1 >= U1) break;
+    const int u2 = grab(ctr);
+    dn_unit_rows(P, S, u2 < U1 ? u2 : u1, A);
+    if (!dn_unit_work(P, S, tag, u1, B, h, ha, hb)) return false;
+    if (u2 >= U1) break;
+    u0 = u2;
+  }
+  return true;
+}
+
 template <int MM>
-__device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
-  // one token per pass keeps h, two row buffers and the decode in registers
-  return down_waves<MM, 1, (MM == 1 ? 8 : 2)>(P, S, tag, gw, NW);
+__device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  if (MM == 1) return down_waves_dyn(P, S, tag, wg, G);
+  return down_waves_static<MM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
+}
+
+// Workgroup work counters of the expert steps: the first row pair / down unit
+// of the workgroup's range.  All threads; ends with a barrier.
+__device__ __forceinline__ void set_counters(const Params& P, const Smem& S, int wg, int G) {
+  if (threadIdx.x == 0) {
+    const int na = S.misc[0];
+    int q0, q1;
+    work_range(S.cgu, na, P.F, wg, G, q0, q1);
+    S.misc[1] = q0;
+    work_range(S.cdn, na, P.d / kDnRows, wg, G, q0, q1);
+    S.misc[2] = q0;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------- combine ---------
@@ -849,7 +1050,7 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
         if (c < P.d) *reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c) = make_float2(a0, a1);
         break;
       }
-      if (!keep_waiting(P, tag, t0, kSiteY, u, round)) return false;
+      if (!keep_waiting(P, tag, t0, kSiteY, u, round, 3)) return false;
     }
   }
   return true;
@@ -858,7 +1059,7 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
 // ---------------------------------------------------------- kernels ---------
 
 // The whole layer in one launch.  SMALL: x of all tokens resident in LDS and
-// top-k computed redundantly in every workgroup.  MM: W_down chunks per lane.
+// top-k published once per token.  MM: W_down chunks per lane.
 template <bool SMALL, int MM>
 __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   extern __shared__ __align__(16) char smem[];
@@ -867,27 +1068,38 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   const int wg = blockIdx.x, G = gridDim.x;
   const int gw = wg * kWaves + uni(threadIdx.x / kWave), NW = G * kWaves;
   const uint32_t tag = start_call(P, wg, true);
+  stamp(P, wg, 0);
   if (threadIdx.x == 0) s_ok = 1;
-  router_step(P, tag, gw, NW);
-  bool ok;
-  if (SMALL) {
-    stage_x(P, S.xs, P.T, [](int r) { return r; });
-    ok = topk_local(P, S, tag, wg == 0);
-  } else {
-    ok = topk_global(P, tag, gw, NW);
-    __syncthreads();
-    ok = load_topk(P, S, tag) && ok;
-  }
+  if (SMALL)
+    router_step<true>(P, S, tag, wg, G, [&] {
+      stage_x(P, S.xs, P.T, [](int r) { return r; });
+      __syncthreads();
+    });
+  else
+    router_step<false>(P, S, tag, wg, G, [] {});
+  stamp(P, wg, 1);
+  bool ok = topk_publish(P, tag, gw, NW);
+  stamp(P, wg, 7);
+  __syncthreads();
+  ok = load_topk(P, S, tag, wg % kTopkRep) && ok;
   __syncthreads();
   if (!ok) s_ok = 0;
   __syncthreads();
+  stamp(P, wg, 2);
   if (s_ok) {
     build_perm(P, S, wg == 0);
+    set_counters(P, S, wg, G);
+    stamp(P, wg, 3);
     if (SMALL)
-      gate_up_waves(P, S, tag, gw, NW);
+      gate_up_waves(P, S, tag, wg, G);
     else
       gate_up_units(P, S, tag, wg, G);
-    if (down_dispatch<MM>(P, S, tag, gw, NW)) combine_step(P, tag, gw, NW);
+    stamp(P, wg, 4);
+    stamp_gu_wave(P, wg);
+    const bool dn = down_dispatch<MM>(P, S, tag, wg, G);
+    stamp(P, wg, 5);
+    if (dn) combine_step(P, tag, gw, NW);
+    stamp(P, wg, 6);
   }
   __syncthreads();
   if (wg == 0) end_call(P, tag, G);
@@ -896,11 +1108,11 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
 // One launch per step (the per-operator model), same arithmetic.
 __global__ void __launch_bounds__(kWG) k_st_router(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
-  router_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+  router_step<false>(P, Smem{}, tag, blockIdx.x, gridDim.x, [] {});
 }
 __global__ void __launch_bounds__(kWG) k_st_topk(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
-  topk_global(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+  topk_publish(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
 }
 __global__ void __launch_bounds__(kWG) k_st_perm(Params P) {
   extern __shared__ __align__(16) char smem[];
@@ -909,7 +1121,7 @@ __global__ void __launch_bounds__(kWG) k_st_perm(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
-  if (!load_topk(P, S, tag)) s_ok = 0;
+  if (!load_topk(P, S, tag, blockIdx.x % kTopkRep)) s_ok = 0;
   __syncthreads();
   if (s_ok) build_perm(P, S, true);
 }
@@ -921,14 +1133,15 @@ __global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
-  if (!load_topk(P, S, tag)) s_ok = 0;
+  if (!load_topk(P, S, tag, blockIdx.x % kTopkRep)) s_ok = 0;
   __syncthreads();
   if (!s_ok) return;
   build_perm(P, S, false);
   if (SMALL) {
     stage_x(P, S.xs, P.T, [](int r) { return r; });
     __syncthreads();
-    gate_up_waves(P, S, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+    set_counters(P, S, blockIdx.x, gridDim.x);
+    gate_up_waves(P, S, tag, blockIdx.x, gridDim.x);
   } else {
     gate_up_units(P, S, tag, blockIdx.x, gridDim.x);
   }
@@ -941,11 +1154,12 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
-  if (!load_topk(P, S, tag)) s_ok = 0;
+  if (!load_topk(P, S, tag, blockIdx.x % kTopkRep)) s_ok = 0;
   __syncthreads();
   if (!s_ok) return;
   build_perm(P, S, false);
-  down_dispatch<MM>(P, S, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+  set_counters(P, S, blockIdx.x, gridDim.x);
+  down_dispatch<MM>(P, S, tag, blockIdx.x, gridDim.x);
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
@@ -979,7 +1193,8 @@ static int check_dims(const moe_mxfp4_dims* dm, int32_t topk) {
 }
 
 struct Layout {
-  size_t hdr, lgp, tki, tkw, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, total;
+  size_t hdr, lgp, tk, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, trace,
+      total;
 };
 
 static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
@@ -987,9 +1202,8 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
   const size_t T = (size_t)dm->T, E = (size_t)dm->E, TK = T * (size_t)k;
   size_t o = 0;
   L.hdr = o; o = align_up(o + kHdrBytes);
-  L.lgp = o; o = align_up(o + T * E * kRouterParts * 8);
-  L.tki = o; o = align_up(o + TK * 8);
-  L.tkw = o; o = align_up(o + TK * 8);
+  L.lgp = o; o = align_up(o + T * ((E + 1) & ~(size_t)1) * 8);
+  L.tk = o; o = align_up(o + (size_t)kTopkRep * TK * 16);
   L.hq = o; o = align_up(o + TK * (size_t)dm->ffn * 8);
   L.yq = o; o = align_up(o + TK * (size_t)dm->d * 8);
   L.logits = o; o = align_up(o + T * E * 4);
@@ -1000,6 +1214,7 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
   L.pos = o; o = align_up(o + TK * 4);
   L.active = o; o = align_up(o + E * 4);
   L.n_active = o; o = align_up(o + 4);
+  L.trace = o; o = align_up(o + (size_t)kMaxGrid * kTraceSlots * 8);
   L.total = o;
   return L;
 }
@@ -1081,8 +1296,7 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.out = out;
   P.hdr = reinterpret_cast<uint32_t*>(b + L.hdr);
   P.lgp = reinterpret_cast<uint64_t*>(b + L.lgp);
-  P.tki = reinterpret_cast<uint64_t*>(b + L.tki);
-  P.tkw = reinterpret_cast<uint64_t*>(b + L.tkw);
+  P.tk = reinterpret_cast<uint64_t*>(b + L.tk);
   P.hq = reinterpret_cast<uint64_t*>(b + L.hq);
   P.yq = reinterpret_cast<uint64_t*>(b + L.yq);
   P.logits = reinterpret_cast<float*>(b + L.logits);
@@ -1093,6 +1307,7 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.pos = reinterpret_cast<int32_t*>(b + L.pos);
   P.active = reinterpret_cast<int32_t*>(b + L.active);
   P.n_active = reinterpret_cast<int32_t*>(b + L.n_active);
+  P.trace = nullptr;
   const uint64_t us = spin_us ? spin_us : 2000000u;
   P.spin_ticks = us * di.ticks_per_us;
   P.withhold = 0;
@@ -1202,6 +1417,7 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxf
   out->n_active = L.n_active;
   out->h = L.hq;
   out->y = L.yq;
+  out->trace = L.trace;
   out->total = L.total;
   return MOE_OK;
 }
@@ -1233,7 +1449,7 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
                          void* workspace, size_t workspace_bytes, const moe_mxfp4_options* opts, void* stream) {
   int st = check_dims(dims, topk);
   if (st != MOE_OK) return st;
-  if (opts && (opts->flags & ~MOE_OPT_WITHHOLD_ARRIVAL)) return MOE_EINVAL;
+  if (opts && (opts->flags & ~(MOE_OPT_WITHHOLD_ARRIVAL | MOE_OPT_TRACE))) return MOE_EINVAL;
   if (opts && opts->grid < 0) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;  // nothing to do; buffers may be empty (null)
   st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
@@ -1248,6 +1464,8 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
   Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di,
                          opts ? opts->spin_limit_us : 0u);
   if (opts && (opts->flags & MOE_OPT_WITHHOLD_ARRIVAL)) P.withhold = 1;
+  if (opts && (opts->flags & MOE_OPT_TRACE))
+    P.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + make_layout(dims, topk).trace);
   const int grid = grid_for(di, layer_kernel(L.small, L.mm), L.lds, opts ? opts->grid : 0);
   return launch_layer(P, L, grid, (hipStream_t)stream);
 }
