@@ -57,6 +57,33 @@ __device__ __forceinline__ float dot32_bf16(const u32x4_t w, float scale, const 
   return acc;
 }
 
+// 32 packed codes (one 16-byte chunk) -> 16 bf16 pairs times the block scale
+// (pair i = elements 2i, 2i+1), for reuse against several tokens.
+__device__ __forceinline__ void decode32_bf16(const u32x4_t w, float scale, bf16x2_t (&v)[16]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[4 * q + 0] = fp4x2_to_bf16x2<0>(ws[q], scale);
+    v[4 * q + 1] = fp4x2_to_bf16x2<1>(ws[q], scale);
+    v[4 * q + 2] = fp4x2_to_bf16x2<2>(ws[q], scale);
+    v[4 * q + 3] = fp4x2_to_bf16x2<3>(ws[q], scale);
+  }
+}
+
+// acc + the 16 decoded pairs against 32 bf16 activations held as four 16-byte
+// pieces, in the same order as dot32_bf16 (so the sums are identical).
+__device__ __forceinline__ float dot32_bf16_dec(const bf16x2_t (&v)[16], const u32x4_t* xq, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t xv = xq[q];
+    acc = dot2_bf16(v[4 * q + 0], xv.x, acc);
+    acc = dot2_bf16(v[4 * q + 1], xv.y, acc);
+    acc = dot2_bf16(v[4 * q + 2], xv.z, acc);
+    acc = dot2_bf16(v[4 * q + 3], xv.w, acc);
+  }
+  return acc;
+}
+
 // 32 packed codes (one 16-byte chunk) -> 32 fp32 values times the block scale.
 __device__ __forceinline__ void decode32_f32(const u32x4_t w, float scale, float (&v)[32]) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};

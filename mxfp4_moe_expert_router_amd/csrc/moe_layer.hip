@@ -72,6 +72,7 @@ constexpr int kMaxF = 4096;
 constexpr int kGUChunks = 4;           // 16-byte chunks per lane of a d-row (d <= 8192)
 constexpr int kRowsGU = 16;            // rows per workgroup unit (large batches)
 constexpr int kMaxTokLds = 8;          // token rows per x staging pass (large batches)
+constexpr int kGUTok = 4;              // tokens per pass over a decoded gate/up row pair
 constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
 constexpr int kMaxGrid = 2048;
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
@@ -490,11 +491,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 }
 
 // Work model of the expert steps, per row of an expert with n tokens (from
-// per-wave timings on MI355X): a gate/up row pair costs 16 + 3 per extra
-// token (the weights are read once, the decode and dot products repeat);
+// per-workgroup timings on MI355X): a gate/up row pair costs 16 + 5 per extra
+// token (the weights are read and decoded once, the dot products repeat);
 // a W_down row costs 10 per pass over the row plus 4 for the second token of
 // a two-token pass (F <= 2048 takes tokens two at a time).
-__device__ __forceinline__ int gu_cost(int n) { return 16 + 3 * (n - 1); }
+__device__ __forceinline__ int gu_cost(int n) { return 16 + 5 * (n - 1); }
 __device__ __forceinline__ int dn_cost(int n, int F) { return F <= 2048 ? 14 * (n / 2) + 10 * (n % 2) : 10 * n; }
 
 // Index, in the (active expert, row) list with R rows per expert, of the
@@ -710,20 +711,52 @@ __device__ __forceinline__ void gu_dot(const Params& P, const u32x4_t* xs, int x
 
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
-// Small batches: x of every token resident in LDS (row t = token t).
+// Small batches: x of every token resident in LDS (row t = token t).  Each
+// chunk of the row pair is decoded once and used for up to kGUTok tokens.
 __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem& S, uint32_t tag, int rho,
                                                     const GURow& R) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int NCH = P.d / 32;
   const int a = uni(rho / P.F), i = uni(rho % P.F);
   const int e = uni(S.act[a]);
   const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
-  for (int tt = 0; tt < ne; ++tt) {
-    const int t = uni(S.slot[p0 + tt]) / P.k;
-    float g = 0.f, u = 0.f;
-    gu_dot(P, S.xs, t, R, g, u);
-    g = wave_sum(g);
-    u = wave_sum(u);
-    if (lane == 0) st_tagged(&P.hq[(size_t)(p0 + tt) * P.F + i], __builtin_bit_cast(uint32_t, swiglu(g, u)), tag);
+  for (int tb = 0; tb < ne; tb += kGUTok) {
+    const int nb = min(kGUTok, ne - tb);
+    float g[kGUTok], u[kGUTok];
+    int xrow[kGUTok];
+#pragma unroll
+    for (int t = 0; t < kGUTok; ++t) {
+      g[t] = u[t] = 0.f;
+      xrow[t] = t < nb ? uni(S.slot[p0 + tb + t]) / P.k : 0;
+    }
+#pragma unroll
+    for (int m = 0; m < kGUChunks; ++m) {
+      if (kWave * m < NCH) {  // uniform; lanes past the row end have scale 0
+        bf16x2_t dg[16], du[16];
+        decode32_bf16(R.g[m], e8m0_to_f32(R.sg[m]), dg);
+        decode32_bf16(R.u[m], e8m0_to_f32(R.su[m]), du);
+        const int cc = min(lane + kWave * m, NCH - 1);
+#pragma unroll
+        for (int t = 0; t < kGUTok; ++t) {
+          if (t < nb) {
+            const u32x4_t* xb = S.xs + (size_t)xrow[t] * 4 * NCH;
+            u32x4_t xq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + cc];
+            g[t] = dot32_bf16_dec(dg, xq, g[t]);
+            u[t] = dot32_bf16_dec(du, xq, u[t]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kGUTok; ++t) {
+      if (t < nb) {
+        const float gs = wave_sum(g[t]), us = wave_sum(u[t]);
+        if (lane == 0)
+          st_tagged(&P.hq[(size_t)(p0 + tb + t) * P.F + i], __builtin_bit_cast(uint32_t, swiglu(gs, us)), tag);
+      }
+    }
   }
 }
 
