@@ -115,8 +115,8 @@ int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stre
 
 /* The whole layer in ONE persistent kernel launch ([P3-PK], [P5-TRT]): router,
  * top-k, permutation, expert gate/up+SwiGLU, down projection and combine.
- * The grid is one workgroup per CU, all co-resident (cooperative launch); the
- * steps hand data to each other through epoch-tagged words that consumers
+ * The grid is one workgroup per CU, all co-resident (see MOE_OPT_COOPERATIVE);
+ * the steps hand data to each other through epoch-tagged words that consumers
  * poll, so no host round trip, grid barrier or device-wide atomic separates
  * them.  The MoE gate is [P1-FP4]/[P3-FP4]'s higher-precision router; the
  * experts are [P5-FP4]'s MXFP4 gate/up/down.
@@ -164,6 +164,14 @@ typedef struct {
  * 5 down, 6 combine; 9-15 the gate/up end of waves 1-7 (slot 4 is wave 0's).
  * Costs one store per step and workgroup. */
 #define MOE_OPT_TRACE 0x2u
+
+/* Launch the persistent kernel cooperatively (hipLaunchCooperativeKernel):
+ * the runtime then guarantees that all its workgroups are resident at once.
+ * By default the kernel is launched normally, which on MI355X saves ~17 us per
+ * call; its grid (one workgroup per CU, each filling its CU) is then resident
+ * at once as long as no other kernel holds CUs, and if one does, the layer's
+ * waits end with MOE_ETIMEOUT instead of hanging. */
+#define MOE_OPT_COOPERATIVE 0x4u
 
 /* moe_mxfp4_forward with options (opts may be NULL). */
 int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ETIMEOUT, MOE_EDEVICE, MOE_EALIGN = range(8)
 MOE_OPT_WITHHOLD_ARRIVAL = 0x1
 MOE_OPT_TRACE = 0x2
+MOE_OPT_COOPERATIVE = 0x4
 
 
 class MoeError(RuntimeError):

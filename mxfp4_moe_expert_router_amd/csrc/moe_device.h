@@ -84,6 +84,34 @@ __device__ __forceinline__ float dot32_bf16_dec(const bf16x2_t (&v)[16], const u
   return acc;
 }
 
+// ---- MFMA operands (v_mfma_f32_16x16x32_bf16, wave64) ----
+// A (16 x 32): lane l holds row l % 16, K elements 8(l / 16) .. +8.
+// B (32 x 16): lane l holds column l % 16, K elements 8(l / 16) .. +8.
+// D (16 x 16, fp32): lane l holds column l % 16, rows 4(l / 16) .. +4.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte chunk (32 codes, one scale block) -> four A operands: operand s
+// holds elements 8s .. 8s+7 of the chunk, times the block scale (exact).
+__device__ __forceinline__ void decode_chunk_a(const u32x4_t w, float scale, bf16x8_t (&a)[4]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x2_t p0 = fp4x2_to_bf16x2<0>(ws[s], scale), p1 = fp4x2_to_bf16x2<1>(ws[s], scale);
+    const bf16x2_t p2 = fp4x2_to_bf16x2<2>(ws[s], scale), p3 = fp4x2_to_bf16x2<3>(ws[s], scale);
+    a[s] = bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  }
+}
+
+// fp32 -> bf16 hi + bf16 lo with hi + lo = v to 16 significant bits (RNE both).
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+
 // 32 packed codes (one 16-byte chunk) -> 32 fp32 values times the block scale.
 __device__ __forceinline__ void decode32_f32(const u32x4_t w, float scale, float (&v)[32]) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};

@@ -16,8 +16,8 @@
 //  [P5-TRT] same page, section "3. TileRT 的"持久化内核"到底做了什么": MoE gate then
 //           expert compute inside one resident kernel.
 //
-// Execution model.  The whole layer is ONE cooperative launch whose grid is
-// one 512-thread workgroup per CU (all co-resident).  Steps hand data to each
+// Execution model.  The whole layer is ONE launch whose grid is one
+// 512-thread workgroup per CU (all co-resident).  Steps hand data to each
 // other through epoch-tagged words: a 64-bit {value, tag} written and read
 // with single-copy-atomic, agent-coherent accesses.  A consumer spins (with a
 // wall-clock watchdog) until the words it needs carry the current call's tag.
@@ -70,14 +70,23 @@ constexpr int kMaxK = 64;
 constexpr int kMaxD = 8192;
 constexpr int kMaxF = 4096;
 constexpr int kGUChunks = 4;           // 16-byte chunks per lane of a d-row (d <= 8192)
-constexpr int kRowsGU = 16;            // rows per workgroup unit (large batches)
-constexpr int kMaxTokLds = 8;          // token rows per x staging pass (large batches)
 constexpr int kGUTok = 4;              // tokens per pass over a decoded gate/up row pair
 constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
 constexpr int kMaxGrid = 2048;
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
 constexpr int kTraceSlots = 16;        // wall-clock stamps per workgroup (trace option)
 constexpr int kTopkRep = 8;            // copies of the top-k results (each read by 1/8 of the grid)
+// MFMA expert path (x does not fit in LDS)
+constexpr int kKB = 128;               // K elements per block
+constexpr int kDnTiles = 4;            // W_down tiles (16 rows) per wave
+constexpr int kGUPass = 32;            // tokens per gate/up pass (2 groups of 16)
+constexpr int kDnPass = 32;            // tokens per down pass (2 groups of 16)
+constexpr int kTileRow = 272;          // LDS bytes per token row of an activation tile (256 + 16 pad)
+constexpr int kGUK = 4;                // gate/up K blocks per step (8 KiB of codes per wave)
+constexpr int kDnK = 1;                // down K blocks per step (4 KiB of codes per wave)
+constexpr int kGUUnitRows = kWaves * 16;             // 128 row pairs
+constexpr int kDnUnitRows = kWaves * kDnTiles * 16;  // 512 rows
+constexpr size_t kMfmaLds = 2 * (size_t)kGUK * kGUPass * kTileRow;  // two activation tiles of a step
 
 // Header words (first kHdrBytes of the workspace).
 enum { kEpoch = 0, kStatus = 1, kAbort = 2, kWhere = 3, kWhat = 4, kStarted = 64 };
@@ -106,7 +115,7 @@ struct Params {
   uint64_t* trace;    // [grid][kTraceSlots] wall-clock stamps, or null
   uint64_t spin_ticks;
   uint32_t withhold;  // test knob: top-k waits for a tag the router never writes
-  int ntl;            // tokens per x staging pass (large batches)
+  int mfma;           // 1: x does not fit in LDS, expert steps on MFMA
 };
 
 // ------------------------------------------------------------ LDS layout ----
@@ -117,7 +126,7 @@ struct LdsPlan {
 
 __host__ __device__ inline size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-__host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool small, int ntl) {
+__host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool small) {
   LdsPlan L;
   const size_t TK = (size_t)T * k;
   const size_t W = ((size_t)T + 63) / 64;
@@ -128,8 +137,9 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool sma
     L.xs = o; o = al16(o + (size_t)T * d * 2);
     L.mask = o; o = al16(o + mask_bytes);
   } else {
-    // x is staged after the permutation is built: the masks alias the x region
-    size_t xs_bytes = (size_t)ntl * d * 2;
+    // the activation tiles of the MFMA path are used after the permutation is
+    // built: the masks alias them
+    size_t xs_bytes = kMfmaLds;
     if (mask_bytes > xs_bytes) xs_bytes = mask_bytes;
     L.xs = o; L.mask = o; o = al16(o + xs_bytes);
   }
@@ -158,9 +168,8 @@ struct Smem {
   int* misc;  // [0] n_active, [8..8+kWaves) scan scratch
 };
 
-// `ntl`: x staging rows of the kernel's layout (0 if it stages no x).
-__device__ __forceinline__ Smem carve(char* base, const Params& P, bool small, int ntl) {
-  const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small, ntl);
+__device__ __forceinline__ Smem carve(char* base, const Params& P, bool small) {
+  const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small);
   Smem S;
   S.xs = reinterpret_cast<u32x4_t*>(base + L.xs);
   S.mask = reinterpret_cast<uint64_t*>(base + L.mask);
@@ -200,7 +209,9 @@ __device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag, uin
 // reused from registers.
 __device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint64_t t0, uint32_t site,
                                              uint32_t what, int& round, int max_shift) {
-  if (aborted(P, tag)) return false;
+  // the abort word (another wait timed out) is a round trip to memory: look
+  // at it every 8th round only
+  if ((round & 7) == 7 && aborted(P, tag)) return false;
   if (wall_clock64() - t0 > P.spin_ticks) {
     raise_timeout(P, tag, site, what);
     return false;
@@ -498,6 +509,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 __device__ __forceinline__ int gu_cost(int n) { return 16 + 5 * (n - 1); }
 __device__ __forceinline__ int dn_cost(int n, int F) { return F <= 2048 ? 14 * (n / 2) + 10 * (n % 2) : 10 * n; }
 
+// Work model of the MFMA path, per workgroup unit of an expert with n tokens:
+// weights stream at HBM speed until the MFMA work of a pass (its column
+// groups ng) exceeds it.
+__device__ __forceinline__ int gu_cost_mfma(int n) {
+  int c = 0;
+  for (int p = 0; p < n; p += kGUPass) c += max(6, 2 * ((min(kGUPass, n - p) + 15) / 16));
+  return c;
+}
+__device__ __forceinline__ int dn_cost_mfma(int n) {
+  int c = 0;
+  for (int p = 0; p < n; p += kDnPass) c += max(10, 7 * ((min(kDnPass, n - p) + 15) / 16));
+  return c;
+}
+
+
 // Index, in the (active expert, row) list with R rows per expert, of the
 // first row whose modelled start lies at or after work position c (c in
 // [0, R * cum[na]]).  cum: cumulative work per row of the active experts.
@@ -586,8 +612,8 @@ __device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool 
     for (int i = 0; i < 2; ++i) {
       const int a = e0 + i;
       const int n = a < na ? S.off[S.act[a] + 1] - S.off[S.act[a]] : 0;
-      g2[i] = a < na ? gu_cost(n) : 0;
-      d2[i] = a < na ? dn_cost(n, P.F) : 0;
+      g2[i] = a < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n)) : 0;
+      d2[i] = a < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
       gs += g2[i];
       ds += d2[i];
     }
@@ -793,40 +819,6 @@ __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, ui
     if (r2 >= Q1) break;
     r0 = r2;
   }
-}
-
-// Large batches: workgroup units (active expert, kRowsGU row pairs); the
-// expert's tokens are staged into LDS P.ntl rows at a time.  All threads.
-__device__ __forceinline__ void gate_up_units(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int F = P.F;
-  const int upe = (F + kRowsGU - 1) / kRowsGU;
-  const int nunits = S.misc[0] * upe;
-  for (int u = wg; u < nunits; u += G) {
-    const int a = u / upe, tile = u % upe;
-    const int e = S.act[a];
-    const int p0 = S.off[e], ne = S.off[e + 1] - p0;
-    const int i0 = tile * kRowsGU, i1 = min(F, i0 + kRowsGU);
-    for (int tg = 0; tg < ne; tg += P.ntl) {
-      const int ntok = min(P.ntl, ne - tg);
-      __syncthreads();
-      stage_x(P, S.xs, ntok, [&](int r) { return S.slot[p0 + tg + r] / P.k; });
-      __syncthreads();
-      for (int i = i0 + wave; i < i1; i += kWaves) {
-        GURow R;
-        gu_load(P, S, a * F + i, R);
-        for (int tt = 0; tt < ntok; ++tt) {
-          float g = 0.f, uu = 0.f;
-          gu_dot(P, S.xs, tt, R, g, uu);
-          g = wave_sum(g);
-          uu = wave_sum(uu);
-          if (lane == 0)
-            st_tagged(&P.hq[(size_t)(p0 + tg + tt) * F + i], __builtin_bit_cast(uint32_t, swiglu(g, uu)), tag);
-        }
-      }
-    }
-  }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------ down ----------
@@ -1056,6 +1048,451 @@ __device__ __forceinline__ void set_counters(const Params& P, const Smem& S, int
   __syncthreads();
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads (HIP's __syncthreads also
+// waits for every global load in flight, which would drain the weight
+// prefetch at every K block).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ------------------------------------ large batches: MFMA expert steps -----
+// When x does not fit in LDS the expert GEMMs run on v_mfma_f32_16x16x32_bf16:
+// A = weights decoded exactly to bf16 (E2M1 * 2^k is a bf16), B = activations
+// as bf16: x exactly, h as hi + lo bf16 (two MFMAs, ~16 significant bits).
+// A workgroup unit covers 8 wave tiles of rows of one expert; its waves walk
+// the K blocks of 128 in lockstep, and the activation tile of each K block
+// (all of the unit's tokens in this pass) is staged once in LDS for all of
+// them.  A K block is one 16-byte code chunk per lane: lane l holds row
+// l % 16, chunk 4j + l / 16, i.e. K elements 128j + 32(l/16) .. +32; MFMA
+// step s uses elements 8s .. 8s+7 of it, and B supplies the same K elements
+// (128j + 32(l/16) + 8s .. +8) for column l % 16, so each MFMA sums a
+// permuted but matching set of 32 K indices.
+
+// Position in a workgroup's stream of (unit, token pass, K block).
+struct Seg {
+  int u, pass, j;   // unit index, first token of the pass, K block
+  int e, p0, ne;    // expert, its first pair, its tokens
+  bool valid;
+};
+
+__device__ __forceinline__ void seg_unit(const Smem& S, int u, int R, Seg& c) {
+  c.u = u;
+  c.pass = 0;
+  c.j = 0;
+  c.e = uni(S.act[u / R]);
+  c.p0 = uni(S.off[c.e]);
+  c.ne = uni(S.off[c.e + 1]) - c.p0;
+}
+
+__device__ __forceinline__ void seg_start(const Smem& S, int U0, int U1, int R, Seg& c) {
+  c.valid = U0 < U1;
+  if (c.valid) seg_unit(S, U0, R, c);
+}
+
+__device__ __forceinline__ void seg_next(const Smem& S, int U1, int R, int nkb, int pass_len, Seg& c) {
+  if (!c.valid) return;
+  if (++c.j < nkb) return;
+  c.j = 0;
+  c.pass += pass_len;
+  if (c.pass < c.ne) return;
+  if (c.u + 1 < U1) seg_unit(S, c.u + 1, R, c);
+  else c.valid = false;
+}
+
+// Number of positions (unit, pass, K block) in units [U0, U1).
+__device__ __forceinline__ int seg_count(const Smem& S, int U0, int U1, int R, int nkb, int pass_len) {
+  int n = 0;
+  for (int u = U0; u < U1; ++u) {
+    const int e = uni(S.act[u / R]);
+    const int ne = uni(S.off[e + 1]) - uni(S.off[e]);
+    n += (ne + pass_len - 1) / pass_len;
+  }
+  return n * nkb;
+}
+
+// ---- gate/up ----
+// Both expert steps move through their stream one step at a time: the x (or
+// h) tile of the next step is loaded first, then the next step's weights, then
+// the current step is computed from registers and LDS, then the next tile is
+// written to LDS and the workgroup synchronises.  Waiting for the next tile
+// therefore never waits for the next step's weights (loads complete in issue
+// order), and each wave keeps 8 KiB of weights in flight while it computes.
+
+// ---- gate/up ----
+struct GUA {
+  u32x4_t g[kGUK], u[kGUK];
+  uint32_t sg[kGUK], su[kGUK];  // scale bytes as loaded
+  uint32_t keep;                // bit b: K block b's chunk is in range
+};
+
+// This wave's tile of step c: rows (u % R) * 128 + 16 * wave + l % 16 of
+// W_gate and W_up, chunks 4(kGUK j + b) + l / 16.  Rows past F (last unit of
+// an expert) and chunks past d read a valid chunk and get a zero scale at use.
+// Nothing is computed from the loaded data here, so the loads stay in flight.
+__device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int R, GUA& A) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d = P.d, F = P.F, NCH = d / 32;
+  const int row = (c.u % R) * kGUUnitRows + 16 * wave + (lane & 15);
+  const int rr = min(row, F - 1);
+  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
+  const uint8_t* pg = P.packed + (size_t)c.e * pbytes + (size_t)rr * (d / 2);
+  const uint8_t* sg = P.scales + (size_t)c.e * sbytes + (size_t)rr * NCH;
+  A.keep = 0;
+#pragma unroll
+  for (int b = 0; b < kGUK; ++b) {
+    const int ch = 4 * (c.j * kGUK + b) + (lane >> 4);
+    const int cc = min(ch, NCH - 1);
+    A.g[b] = ld_stream16(pg + (size_t)cc * 16);
+    A.u[b] = ld_stream16(pg + (size_t)F * d / 2 + (size_t)cc * 16);
+    A.sg[b] = sg[cc];
+    A.su[b] = sg[(size_t)F * NCH + cc];
+    A.keep |= (row < F && ch < NCH) ? 1u << b : 0u;
+  }
+}
+
+// x tile of step c: token rows n < 32 of the pass, K blocks kGUK j .. +kGUK,
+// four 16-byte pieces per thread; LDS layout [block][token][272 bytes].
+// `ok` bit m marks pieces that hold data (others are written as zeros).
+constexpr int kXPieces = kGUK * kGUPass * 16 / kWG;
+static_assert(kGUK == 4 && kXPieces == 4, "piece index = token(5) | block(2) | piece(4) bits");
+__device__ __forceinline__ void gu_mfma_xload(const Params& P, const Smem& S, const Seg& c,
+                                              u32x4_t (&v)[kXPieces], uint32_t& ok) {
+  const int TK = P.T * P.k;
+  const int np = min(kGUPass, c.ne - c.pass);
+  const int tok = uni(S.slot[min(c.p0 + c.pass, TK - 1)]) / P.k;  // a valid row for the clamped reads
+  ok = 0;
+#pragma unroll
+  for (int m = 0; m < kXPieces; ++m) {
+    const int pc = (int)threadIdx.x + kWG * m;
+    const int n = pc >> 6, b = (pc >> 4) & 3, q = pc & 15;
+    const int kk = (c.j * kGUK + b) * kKB + 8 * q;
+    const bool use = c.valid && n < np && kk < P.d;
+    const int t = use ? S.slot[min(c.p0 + c.pass + n, TK - 1)] / P.k : tok;
+    v[m] = *reinterpret_cast<const u32x4_t*>(P.x + (size_t)t * P.d + min(kk, P.d - 8));
+    ok |= use ? 1u << m : 0u;
+  }
+}
+
+__device__ __forceinline__ void gu_mfma_xstore(char* tile, const u32x4_t (&v)[kXPieces], uint32_t ok) {
+#pragma unroll
+  for (int m = 0; m < kXPieces; ++m) {
+    const int pc = (int)threadIdx.x + kWG * m;
+    const int n = pc >> 6, b = (pc >> 4) & 3, q = pc & 15;
+    *reinterpret_cast<u32x4_t*>(tile + (b * kGUPass + n) * kTileRow + q * 16) =
+        (ok >> m) & 1u ? v[m] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// MFMAs of one step for this wave's tile against the x tile in LDS, for the
+// first NG column groups of 16 tokens.
+template <int NG>
+__device__ __forceinline__ void gu_mfma_step(const GUA& A, const char* tile, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const char* b0 = tile + (lane & 15) * kTileRow + (lane >> 4) * 64;
+#pragma unroll
+  for (int b = 0; b < kGUK; ++b) {
+    bf16x8_t x[4][NG];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        x[s][g] = *reinterpret_cast<const bf16x8_t*>(b0 + (b * kGUPass + g * 16) * kTileRow + s * 16);
+    const bool in = (A.keep >> b) & 1u;
+    bf16x8_t wg[4], wu[4];
+    decode_chunk_a(A.g[b], e8m0_to_f32(in ? A.sg[b] : 0u), wg);
+    decode_chunk_a(A.u[b], e8m0_to_f32(in ? A.su[b] : 0u), wu);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        ag[g] = mfma_bf16(wg[s], x[s][g], ag[g]);
+        au[g] = mfma_bf16(wu[s], x[s][g], au[g]);
+      }
+    }
+  }
+}
+
+// h = silu(g) * u of this wave's tile for the pass's tokens, as tagged words.
+__device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int R, uint32_t tag, f32x4_t (&ag)[2],
+                                              f32x4_t (&au)[2]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int np = min(kGUPass, c.ne - c.pass);
+  const int row0 = (c.u % R) * kGUUnitRows + 16 * wave;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int n = 16 * g + (lane & 15);
+    if (row0 < P.F && n < np) {
+      uint64_t* hp = P.hq + (size_t)(c.p0 + c.pass + n) * P.F + row0 + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_tagged(hp + i, __builtin_bit_cast(uint32_t, swiglu(ag[g][i], au[g][i])), tag);
+    }
+    ag[g] = au[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One step: prefetch the next step (x tile into registers, weights into An),
+// compute the current one (Ac, LDS tile `cur`), write the next tile into LDS
+// tile `nxt`, synchronise.  Returns false when the stream is done.
+__device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+                                            int q, int npos, Seg& cc, Seg& nc, const GUA& Ac, GUA& An, char* cur,
+                                            char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
+  u32x4_t xr[kXPieces];
+  uint32_t xok;
+  gu_mfma_xload(P, S, nc, xr, xok);  // first: waiting for it below must not wait for An
+  gu_mfma_load(P, nc, R, An);
+  if (cc.ne - cc.pass > 16)
+    gu_mfma_step<2>(Ac, cur, ag, au);
+  else
+    gu_mfma_step<1>(Ac, cur, ag, au);
+  if (cc.j == nst - 1) gu_mfma_store(P, cc, R, tag, ag, au);
+  if (q + 1 < npos) gu_mfma_xstore(nxt, xr, xok);
+  seg_next(S, U1, R, nst, kGUPass, cc);
+  seg_next(S, U1, R, nst, kGUPass, nc);
+  lds_barrier();
+}
+
+// Gate/up + SwiGLU for the workgroup's units [U0, U1) (equal shares of the
+// modelled work).  All threads of the workgroup.
+__device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  const int R = (P.F + kGUUnitRows - 1) / kGUUnitRows;
+  const int nst = (P.d + kGUK * kKB - 1) / (kGUK * kKB);
+  int U0, U1;
+  work_range(S.cgu, uni(S.misc[0]), R, wg, G, U0, U1);
+  const int npos = seg_count(S, U0, U1, R, nst, kGUPass);
+  if (npos == 0) return;
+  char* t0 = reinterpret_cast<char*>(S.xs);
+  char* t1 = t0 + kGUK * kGUPass * kTileRow;
+  Seg cc, nc;
+  seg_start(S, U0, U1, R, cc);
+  nc = cc;
+  GUA A0, A1;
+  f32x4_t ag[2], au[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) ag[g] = au[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  {
+    u32x4_t xr[kXPieces];
+    uint32_t xok;
+    gu_mfma_xload(P, S, nc, xr, xok);
+    gu_mfma_load(P, nc, R, A0);
+    gu_mfma_xstore(t0, xr, xok);
+    seg_next(S, U1, R, nst, kGUPass, nc);
+    lds_barrier();
+  }
+  for (int q = 0; q < npos; q += 2) {
+    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, nc, A0, A1, t0, t1, ag, au);
+    if (q + 1 >= npos) break;
+    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, nc, A1, A0, t1, t0, ag, au);
+  }
+}
+
+// ---- down ----
+struct DnA {
+  u32x4_t w[kDnK][kDnTiles];
+  uint32_t s[kDnK][kDnTiles];  // scale bytes as loaded
+  uint32_t keep;               // bit b * kDnTiles + t: in range
+};
+
+// This wave's 4 tiles of step c: rows (u % R) * 512 + 64 * wave + 16t + l % 16
+// of W_down, chunks 4(kDnK j + b) + l / 16 (K = F).
+__device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int R, DnA& A) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d = P.d, F = P.F, NCH = F / 32;
+  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
+  const uint8_t* pd = P.packed + (size_t)c.e * pbytes + (size_t)F * d;
+  const uint8_t* sd = P.scales + (size_t)c.e * sbytes + (size_t)F * d / 16;
+  A.keep = 0;
+#pragma unroll
+  for (int b = 0; b < kDnK; ++b) {
+    const int ch = 4 * (c.j * kDnK + b) + (lane >> 4);
+    const int cc = min(ch, NCH - 1);
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) {
+      const int row = (c.u % R) * kDnUnitRows + 64 * wave + 16 * t + (lane & 15);
+      const int rr = min(row, d - 1);
+      A.w[b][t] = ld_stream16(pd + (size_t)rr * (F / 2) + (size_t)cc * 16);
+      A.s[b][t] = sd[(size_t)rr * NCH + cc];
+      A.keep |= (row < d && ch < NCH) ? 1u << (b * kDnTiles + t) : 0u;
+    }
+  }
+}
+
+// h tile of step c: pairs n < 32 of the pass, values 128(kDnK j) .. +128 kDnK
+// as tagged words, 16-byte coherent loads of two words (row n = piece /
+// kHRow, word pair = piece % kHRow).
+constexpr int kHRow = kDnK * kKB / 2;  // word pairs per pair row of a step
+constexpr int kHPieces = kDnPass * kHRow / kWG;
+__device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
+                                              u32x4_t (&v)[kHPieces]) {
+  const int np = max(1, min(kDnPass, c.ne - c.pass));
+#pragma unroll
+  for (int m = 0; m < kHPieces; ++m) {
+    const int pc = (int)threadIdx.x + kWG * m;
+    const int n = min(pc / kHRow, np - 1), k = min(c.j * kDnK * kKB + 2 * (pc % kHRow), P.F - 2);
+    v[m] = ld_coherent16(rs, ((uint32_t)(c.p0 + c.pass + n) * (uint32_t)P.F + (uint32_t)k) * 8u);
+  }
+}
+
+// Checks the tags of a staged h tile (re-reading it until they are current;
+// after a watchdog abort it gives up and the data is not used), then writes it
+// as bf16 hi and lo tiles, layout [block][pair][272 bytes] each.  Values past
+// the pass or past F are zero.
+__device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
+                                               uint32_t tag, u32x4_t (&v)[kHPieces], char* hi_tile,
+                                               char* lo_tile) {
+  const int np = min(kDnPass, c.ne - c.pass);
+  auto used = [&](int m) {
+    const int pc = (int)threadIdx.x + kWG * m;
+    return c.valid && pc / kHRow < np && c.j * kDnK * kKB + 2 * (pc % kHRow) < P.F;
+  };
+  auto current = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < kHPieces; ++m) ok &= !used(m) || (v[m].y == tag && v[m].w == tag);
+    return ok;
+  };
+  if (!__all(current())) {
+    const uint64_t t0 = wall_clock64();
+    int round = 0;
+    for (;;) {
+      if (!keep_waiting(P, tag, t0, kSiteH, c.p0 + c.pass, round, 3)) break;
+      dn_mfma_hload(P, c, rs, v);
+      if (__all(current())) break;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kHPieces; ++m) {
+    const int pc = (int)threadIdx.x + kWG * m;
+    const int n = pc / kHRow, w = pc % kHRow;  // w: word pair within the step's values
+    const int off = ((w >> 6) * kDnPass + n) * kTileRow + (w & 63) * 4;
+    const bool u = used(m);
+    __bf16 h0, l0, h1, l1;
+    split_bf16(u ? u2f(v[m].x) : 0.f, h0, l0);
+    split_bf16(u ? u2f(v[m].z) : 0.f, h1, l1);
+    *reinterpret_cast<bf16x2_t*>(hi_tile + off) = bf16x2_t{h0, h1};
+    *reinterpret_cast<bf16x2_t*>(lo_tile + off) = bf16x2_t{l0, l1};
+  }
+}
+
+// Operand s of a decoded chunk (elements 8s .. 8s+7, times the scale).
+__device__ __forceinline__ bf16x8_t decode_op_a(const u32x4_t w, float scale, int s) {
+  const uint32_t ws = s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
+  const bf16x2_t p0 = fp4x2_to_bf16x2<0>(ws, scale), p1 = fp4x2_to_bf16x2<1>(ws, scale);
+  const bf16x2_t p2 = fp4x2_to_bf16x2<2>(ws, scale), p3 = fp4x2_to_bf16x2<3>(ws, scale);
+  return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+template <int NG>
+__device__ __forceinline__ void dn_mfma_step(const DnA& A, const char* hi_tile, const char* lo_tile,
+                                             f32x4_t (&acc)[kDnTiles][2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int boff = (lane & 15) * kTileRow + (lane >> 4) * 64;
+#pragma unroll
+  for (int b = 0; b < kDnK; ++b) {
+    float sc[kDnTiles];
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) sc[t] = e8m0_to_f32((A.keep >> (b * kDnTiles + t)) & 1u ? A.s[b][t] : 0u);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t bh[NG], bl[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int o = boff + (b * kDnPass + g * 16) * kTileRow + s * 16;
+        bh[g] = *reinterpret_cast<const bf16x8_t*>(hi_tile + o);
+        bl[g] = *reinterpret_cast<const bf16x8_t*>(lo_tile + o);
+      }
+      bf16x8_t a[kDnTiles];
+#pragma unroll
+      for (int t = 0; t < kDnTiles; ++t) a[t] = decode_op_a(A.w[b][t], sc[t], s);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int t = 0; t < kDnTiles; ++t) {
+          acc[t][g] = mfma_bf16(a[t], bh[g], acc[t][g]);
+          acc[t][g] = mfma_bf16(a[t], bl[g], acc[t][g]);
+        }
+      }
+    }
+  }
+}
+
+// gate * y of this wave's 4 tiles for the pass's tokens, as tagged words in
+// the tokens' slot rows.
+__device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, const Seg& c, int R, uint32_t tag,
+                                              f32x4_t (&acc)[kDnTiles][2]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int np = min(kDnPass, c.ne - c.pass);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int n = 16 * g + (lane & 15);
+    const int slot = n < np ? S.slot[min(c.p0 + c.pass + n, P.T * P.k - 1)] : 0;
+    const float gate = n < np ? S.tkw[slot] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kDnTiles; ++t) {
+      const int row0 = (c.u % R) * kDnUnitRows + 64 * wave + 16 * t;
+      if (row0 < P.d && n < np) {
+        uint64_t* yp = P.yq + (size_t)slot * P.d + row0 + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_tagged(yp + i, __builtin_bit_cast(uint32_t, gate * acc[t][g][i]), tag);
+      }
+      acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+__device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+                                            int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
+                                            const DnA& Ac, DnA& An, char* cur, char* nxt,
+                                            f32x4_t (&acc)[kDnTiles][2]) {
+  constexpr int kHalf = kDnK * kDnPass * kTileRow;  // hi tile; lo tile follows
+  u32x4_t hr[kHPieces];
+  dn_mfma_hload(P, nc, rs, hr);  // first: waiting for it below must not wait for An
+  dn_mfma_load(P, nc, R, An);
+  if (cc.ne - cc.pass > 16)
+    dn_mfma_step<2>(Ac, cur, cur + kHalf, acc);
+  else
+    dn_mfma_step<1>(Ac, cur, cur + kHalf, acc);
+  if (cc.j == nst - 1) dn_mfma_store(P, S, cc, R, tag, acc);
+  if (q + 1 < npos) dn_mfma_hstore(P, nc, rs, tag, hr, nxt, nxt + kHalf);
+  seg_next(S, U1, R, nst, kDnPass, cc);
+  seg_next(S, U1, R, nst, kDnPass, nc);
+  lds_barrier();
+}
+
+// Down projection for the workgroup's units [U0, U1).  All threads.
+__device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  const int R = (P.d + kDnUnitRows - 1) / kDnUnitRows;
+  const int nst = (P.F + kDnK * kKB - 1) / (kDnK * kKB);
+  int U0, U1;
+  work_range(S.cdn, uni(S.misc[0]), R, wg, G, U0, U1);
+  const int npos = seg_count(S, U0, U1, R, nst, kDnPass);
+  if (npos == 0) return;
+  constexpr int kHalf = kDnK * kDnPass * kTileRow;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq, (uint32_t)((size_t)P.T * P.k * P.F * 8));
+  char* t0 = reinterpret_cast<char*>(S.xs);
+  char* t1 = t0 + 2 * kHalf;
+  Seg cc, nc;
+  seg_start(S, U0, U1, R, cc);
+  nc = cc;
+  DnA A0, A1;
+  f32x4_t acc[kDnTiles][2];
+#pragma unroll
+  for (int t = 0; t < kDnTiles; ++t) acc[t][0] = acc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  {
+    u32x4_t hr[kHPieces];
+    dn_mfma_hload(P, nc, rs, hr);
+    dn_mfma_load(P, nc, R, A0);
+    dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf);
+    seg_next(S, U1, R, nst, kDnPass, nc);
+    lds_barrier();
+  }
+  for (int q = 0; q < npos; q += 2) {
+    dn_mfma_one(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc);
+    if (q + 1 >= npos) break;
+    dn_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc);
+  }
+}
+
 // ---------------------------------------------------------- combine ---------
 // out[t][c] = sum over j < k of the tagged gated rows y[t*k + j][c], in slot
 // order.  Unit = (token, 64 columns), one wave.
@@ -1097,7 +1534,7 @@ template <bool SMALL, int MM>
 __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_ok;
-  const Smem S = carve(smem, P, SMALL, SMALL ? 0 : P.ntl);
+  const Smem S = carve(smem, P, SMALL);
   const int wg = blockIdx.x, G = gridDim.x;
   const int gw = wg * kWaves + uni(threadIdx.x / kWave), NW = G * kWaves;
   const uint32_t tag = start_call(P, wg, true);
@@ -1123,13 +1560,17 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
     build_perm(P, S, wg == 0);
     set_counters(P, S, wg, G);
     stamp(P, wg, 3);
-    if (SMALL)
+    bool dn = true;
+    if (SMALL) {
       gate_up_waves(P, S, tag, wg, G);
-    else
-      gate_up_units(P, S, tag, wg, G);
-    stamp(P, wg, 4);
-    stamp_gu_wave(P, wg);
-    const bool dn = down_dispatch<MM>(P, S, tag, wg, G);
+      stamp(P, wg, 4);
+      stamp_gu_wave(P, wg);
+      dn = down_dispatch<MM>(P, S, tag, wg, G);
+    } else {
+      gate_up_mfma(P, S, tag, wg, G);
+      stamp(P, wg, 4);
+      down_mfma(P, S, tag, wg, G);
+    }
     stamp(P, wg, 5);
     if (dn) combine_step(P, tag, gw, NW);
     stamp(P, wg, 6);
@@ -1150,7 +1591,7 @@ __global__ void __launch_bounds__(kWG) k_st_topk(Params P) {
 __global__ void __launch_bounds__(kWG) k_st_perm(Params P) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_ok;
-  const Smem S = carve(smem, P, false, 0);
+  const Smem S = carve(smem, P, false);
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
@@ -1162,7 +1603,7 @@ template <bool SMALL>
 __global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_ok;
-  const Smem S = carve(smem, P, SMALL, SMALL ? 0 : P.ntl);
+  const Smem S = carve(smem, P, SMALL);
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
@@ -1176,14 +1617,15 @@ __global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
     set_counters(P, S, blockIdx.x, gridDim.x);
     gate_up_waves(P, S, tag, blockIdx.x, gridDim.x);
   } else {
-    gate_up_units(P, S, tag, blockIdx.x, gridDim.x);
+    gate_up_mfma(P, S, tag, blockIdx.x, gridDim.x);
   }
 }
+// MM: W_down chunks per lane of the small-batch path; 0 = the MFMA path.
 template <int MM>
 __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_ok;
-  const Smem S = carve(smem, P, false, 0);
+  const Smem S = carve(smem, P, false);
   const uint32_t tag = start_call(P, blockIdx.x, false);
   if (threadIdx.x == 0) s_ok = 1;
   __syncthreads();
@@ -1192,7 +1634,10 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   if (!s_ok) return;
   build_perm(P, S, false);
   set_counters(P, S, blockIdx.x, gridDim.x);
-  down_dispatch<MM>(P, S, tag, blockIdx.x, gridDim.x);
+  if (MM == 0)
+    down_mfma(P, S, tag, blockIdx.x, gridDim.x);
+  else
+    down_dispatch<MM == 0 ? 1 : MM>(P, S, tag, blockIdx.x, gridDim.x);
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
@@ -1254,15 +1699,9 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
 
 // x of all tokens fits in LDS next to the permutation tables.
 static bool use_small(const moe_mxfp4_dims* dm, int32_t k) {
-  return lds_plan(dm->T, dm->d, dm->E, k, true, 0).total <= (size_t)kLdsMax;
+  return lds_plan(dm->T, dm->d, dm->E, k, true).total <= (size_t)kLdsMax;
 }
 
-static int tokens_per_pass(const moe_mxfp4_dims* dm, int32_t k) {
-  const size_t fixed = lds_plan(dm->T, 32, dm->E, k, false, 0).total;  // tables (+ mask) only
-  if (fixed + (size_t)dm->d * 2 > (size_t)kLdsMax) return 0;
-  int n = (int)(((size_t)kLdsMax - fixed) / ((size_t)dm->d * 2));
-  return n > kMaxTokLds ? kMaxTokLds : n;
-}
 
 struct DeviceInfo {
   int cus = 0;
@@ -1289,7 +1728,7 @@ static int device_info(DeviceInfo* out) {
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_EDEVICE;
     const void* ks[] = {layer_kernel(true, 1), layer_kernel(true, 2), layer_kernel(false, 1), layer_kernel(false, 2),
                         (const void*)k_st_perm, (const void*)k_st_gate_up<true>, (const void*)k_st_gate_up<false>,
-                        (const void*)k_st_down<1>, (const void*)k_st_down<2>};
+                        (const void*)k_st_down<0>, (const void*)k_st_down<1>, (const void*)k_st_down<2>};
     for (const void* f : ks) {
       if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess) {
         (void)hipGetLastError();  // do not leave a sticky error for the caller's next HIP call
@@ -1344,7 +1783,7 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   const uint64_t us = spin_us ? spin_us : 2000000u;
   P.spin_ticks = us * di.ticks_per_us;
   P.withhold = 0;
-  P.ntl = tokens_per_pass(dm, k);
+  P.mfma = 0;
   return P;
 }
 
@@ -1373,18 +1812,25 @@ static int plan_launch(const moe_mxfp4_dims* dm, int32_t k, Launch* L) {
   L->small = use_small(dm, k);
   L->mm = chunks_per_lane_down(dm);
   if (L->mm < 1 || L->mm > 2) return MOE_ESHAPE;
-  const int ntl = tokens_per_pass(dm, k);
-  if (!L->small && ntl < 1) return MOE_ESHAPE;
-  const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->small, L->small ? 0 : ntl);
+  const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->small);
   if (pl.total > (size_t)kLdsMax) return MOE_ESHAPE;
   L->lds = pl.total;
   return MOE_OK;
 }
 
-static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s) {
+// The layer's waits need every workgroup resident at once.  The grid is at
+// most one workgroup per CU and a workgroup's registers and LDS fill a CU, so
+// on an idle device a plain launch places them all; a cooperative launch
+// guarantees it but costs ~17 us more per call on MI355X (measured: 19 us vs
+// 2.3 us back to back for an empty kernel), so it is an option.  If other work
+// holds CUs, a plain launch's waits time out (MOE_ETIMEOUT) instead of hanging.
+static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s, bool cooperative) {
   void* args[] = {&P};
-  hipError_t e = hipLaunchCooperativeKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args,
-                                            (unsigned)L.lds, s);
+  hipError_t e;
+  if (cooperative)
+    e = hipLaunchCooperativeKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
+  else
+    e = hipLaunchKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return MOE_ELAUNCH;
@@ -1393,7 +1839,7 @@ static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s) {
 }
 
 static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t s, bool experts) {
-  const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, false, 0).total;
+  const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, false).total;
   hipLaunchKernelGGL(k_st_router, dim3(grid), dim3(kWG), 0, s, P);
   hipLaunchKernelGGL(k_st_topk, dim3(grid), dim3(kWG), 0, s, P);
   if (experts) {
@@ -1401,7 +1847,9 @@ static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t
       hipLaunchKernelGGL(k_st_gate_up<true>, dim3(grid), dim3(kWG), (unsigned)L.lds, s, P);
     else
       hipLaunchKernelGGL(k_st_gate_up<false>, dim3(grid), dim3(kWG), (unsigned)L.lds, s, P);
-    if (L.mm == 1)
+    if (!L.small)
+      hipLaunchKernelGGL(k_st_down<0>, dim3(grid), dim3(kWG), lds_tables, s, P);
+    else if (L.mm == 1)
       hipLaunchKernelGGL(k_st_down<1>, dim3(grid), dim3(kWG), lds_tables, s, P);
     else
       hipLaunchKernelGGL(k_st_down<2>, dim3(grid), dim3(kWG), lds_tables, s, P);
@@ -1482,7 +1930,7 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
                          void* workspace, size_t workspace_bytes, const moe_mxfp4_options* opts, void* stream) {
   int st = check_dims(dims, topk);
   if (st != MOE_OK) return st;
-  if (opts && (opts->flags & ~(MOE_OPT_WITHHOLD_ARRIVAL | MOE_OPT_TRACE))) return MOE_EINVAL;
+  if (opts && (opts->flags & ~(MOE_OPT_WITHHOLD_ARRIVAL | MOE_OPT_TRACE | MOE_OPT_COOPERATIVE))) return MOE_EINVAL;
   if (opts && opts->grid < 0) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;  // nothing to do; buffers may be empty (null)
   st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
@@ -1496,11 +1944,12 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
   if (st != MOE_OK) return st;
   Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di,
                          opts ? opts->spin_limit_us : 0u);
+  P.mfma = L.small ? 0 : 1;
   if (opts && (opts->flags & MOE_OPT_WITHHOLD_ARRIVAL)) P.withhold = 1;
   if (opts && (opts->flags & MOE_OPT_TRACE))
     P.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + make_layout(dims, topk).trace);
   const int grid = grid_for(di, layer_kernel(L.small, L.mm), L.lds, opts ? opts->grid : 0);
-  return launch_layer(P, L, grid, (hipStream_t)stream);
+  return launch_layer(P, L, grid, (hipStream_t)stream, opts && (opts->flags & MOE_OPT_COOPERATIVE));
 }
 
 int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
@@ -1526,6 +1975,7 @@ int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const fl
   st = device_info(&di);
   if (st != MOE_OK) return st;
   Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di, 0u);
+  P.mfma = L.small ? 0 : 1;
   return launch_staged(P, L, di.cus, (hipStream_t)stream, true);
 }
 
@@ -1546,6 +1996,7 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
   if (st != MOE_OK) return st;
   // packed/scales/out are not touched by the routing kernels
   Params P = make_params(dims, topk, x, router_w, nullptr, nullptr, nullptr, workspace, di, 0u);
+  P.mfma = L.small ? 0 : 1;
   hipStream_t s = (hipStream_t)stream;
   st = launch_staged(P, L, di.cus, s, false);
   if (st != MOE_OK) return st;

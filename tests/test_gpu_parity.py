@@ -79,8 +79,10 @@ SMALL = [
     dict(T=64, d=1056, F=224, E=4, k=2),       # ~32 tokens per expert: many LDS token passes
     dict(T=33, d=2080, F=2080, E=64, k=8),     # 65 chunks per row: second lane pass of one chunk
     dict(T=5, d=7168, F=2048, E=12, k=3),      # full-width experts, few of them
-    dict(T=40, d=4096, F=128, E=6, k=2),       # x too large to keep resident: staged per token group
-    dict(T=100, d=2048, F=2080, E=16, k=4),    # staged x, two W_down chunks per lane
+    dict(T=40, d=4096, F=128, E=6, k=2),       # x too large for LDS: MFMA expert path
+    dict(T=100, d=2048, F=2080, E=16, k=4),    # MFMA path, F % 128 != 0
+    dict(T=96, d=1024, F=256, E=4, k=2),       # MFMA path: ~48 tokens per expert, two token passes
+    dict(T=100, d=800, F=96, E=3, k=2),        # MFMA path: partial K blocks and partial row units
 ]
 
 
@@ -228,3 +230,17 @@ def test_small_grid_option(env):
         out = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(0, 0, g))
         torch.cuda.synchronize()
         assert rel_err(out.cpu().numpy(), ref.out) <= OUT_TOL, g
+
+
+def test_cooperative_launch_option(env):
+    # the cooperative launch gives the same bits as the default plain launch
+    torch, moe, oracle, synth = env
+    cfg = synth.Config("coop", T=8, d=512, F=256, E=16, k=4)
+    x, wr, p, s = inputs_for(synth, cfg)
+    xt, wrt, pt, st = to_device(torch, x, wr, p, s)
+    a = moe.forward(xt, wrt, pt, st, cfg.k)
+    b = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(moe.MOE_OPT_COOPERATIVE, 0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
+    assert rel_err(b.cpu().numpy(), ref.out) <= OUT_TOL
