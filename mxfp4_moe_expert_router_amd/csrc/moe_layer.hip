@@ -527,31 +527,123 @@ __device__ __forceinline__ int dn_cost_mfma(int n) {
 // Index, in the (active expert, row) list with R rows per expert, of the
 // first row whose modelled start lies at or after work position c (c in
 // [0, R * cum[na]]).  cum: cumulative work per row of the active experts.
-__device__ __forceinline__ int row_at(const int* cum, int na, int R, int64_t c) {
-  const int cq = (int)(c / R);
-  int lo = 0, hi = na;  // largest a with cum[a] <= cq
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uni(cum[mid]) <= cq) lo = mid;
-    else hi = mid - 1;
-  }
+__device__ __forceinline__ int row_at(const int* cum, int na, int R, int w, int G) {
+  // Work position c = floor(R * cum[na] * w / G).  A full wave searches
+  // together for the last active expert starting at or below c: the lanes
+  // sample every 16th entry, then the 17 entries after the last sample at or
+  // below c / R (cum is strictly increasing over [0, na], na <= 1024).
+  // Quotients of exact integers below 2^53 are taken in double precision: the
+  // distance of a non-integer quotient to the next integer is at least 1/G,
+  // far above the rounding error, so the floors are exact.
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t X = (int64_t)uni(cum[na]) * w;
+  const int cq = (int)floor((double)X / (double)G);  // floor(c / R)
+  const uint64_t b1 = __ballot(cum[min(lane * 16, na)] <= cq);  // a prefix of the lanes, lane 0 set
+  const int L = 63 - __clzll(b1);
+  const int i2 = min(L * 16 + lane, na);
+  const uint64_t b2 = __ballot(lane <= 16 && cum[i2] <= cq);
+  const int lo = min(L * 16 + 63 - __clzll(b2), na);
   if (lo >= na) return na * R;
-  const int u = uni(cum[lo + 1]) - uni(cum[lo]);
-  const int64_t rem = c - (int64_t)R * uni(cum[lo]);
-  const int i = (int)((rem + u - 1) / u);
+  const int c0 = uni(cum[lo]);
+  const int u = uni(cum[lo + 1]) - c0;
+  // c - R * cum[lo] = floor(R * (X - G * cum[lo]) / G), with 0 <= X - G * cum[lo] < G * u
+  const int64_t t = (int64_t)R * (X - (int64_t)G * c0);
+  const int rem = (int)floor((double)t / (double)G);
+  const int i = (rem + u - 1) / u;
   return lo * R + min(i, R);
 }
 
-// Rows [q0, q1) of wave gw of NW: equal shares of the modelled work.
-__device__ __forceinline__ void work_range(const int* cum, int na, int R, int gw, int NW, int& q0, int& q1) {
-  const int64_t C = (int64_t)R * uni(cum[na]);
-  q0 = row_at(cum, na, R, C * gw / NW);
-  q1 = row_at(cum, na, R, C * (gw + 1) / NW);
+// Rows [q0, q1) of part w of W: equal shares of the modelled work.  One wave.
+__device__ __forceinline__ void work_range(const int* cum, int na, int R, int w, int W, int& q0, int& q1) {
+  q0 = row_at(cum, na, R, w, W);
+  q1 = row_at(cum, na, R, w + 1, W);
+}
+
+// T*k <= 64: wave 0 alone, one pair per lane.  The position of pair s is the
+// number of pairs of a lower expert plus the pairs of the same expert in lower
+// slots (each token picks an expert once, so lower slot = lower token).
+// Writes what build_perm writes; S.off holds the offsets of the active experts
+// and of the entry after each (the only ones read).  All threads.
+__device__ __forceinline__ void build_perm_wave(const Params& P, const Smem& S, bool debug) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int E = P.E, TK = P.T * P.k;
+  __syncthreads();
+  if (tid < kWave) {
+    const bool valid = lane < TK;
+    const int e = valid ? S.tki[lane] : 0x7FFFFFFF;
+    // rank by expert with ballots over the expert index bits (MSB first):
+    // `eq` keeps the lanes whose bits so far equal this lane's
+    const int nb = 32 - __clz(max(E - 1, 1));
+    uint64_t eq = __ballot(valid);
+    int lower = 0;
+    for (int b = nb - 1; b >= 0; --b) {
+      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      if ((e >> b) & 1) {
+        lower += __popcll(eq & ~ones);
+        eq &= ones;
+      } else {
+        eq &= ~ones;
+      }
+    }
+    const int before = __popcll(eq & ((1ull << lane) - 1ull));
+    const int same = __popcll(eq);
+    const int pos = lower + before;
+    const bool first = valid && before == 0;
+    // mark the first position of every expert, read the marks back as a mask
+    if (valid) {
+      S.slot[pos] = lane;
+      S.cdn[pos] = first ? 1 : 0;  // scratch until the work model below
+    }
+    const uint64_t fm = __ballot(valid && S.cdn[lane] != 0);
+    const int a = __popcll(fm & ((1ull << (pos - before)) - 1ull));  // distinct experts below e
+    const int na = __popcll(fm);
+    if (first) {
+      S.act[a] = e;
+      S.off[e] = pos;
+      S.off[e + 1] = pos + same;  // equal to the next active expert's offset if it is e + 1
+      S.cgu[a] = same;            // token counts by active index, read back below
+    }
+    if (lane == 0) S.misc[0] = na;
+    const int n = lane < na ? S.cgu[lane] : 0;
+    const int g = lane < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n)) : 0;
+    const int dc = lane < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
+    const int gi = wave_inclusive_scan(g), di = wave_inclusive_scan(dc);
+    if (lane < na) {
+      S.cgu[lane] = gi - g;
+      S.cdn[lane] = di - dc;
+    }
+    if (lane == na - 1) {
+      S.cgu[na] = gi;
+      S.cdn[na] = di;
+    }
+    if (debug) {
+      if (valid) {
+        P.pos[lane] = pos;
+        P.sorted_slot[pos] = lane;
+        P.topk_idx[lane] = e;
+        P.topk_w[lane] = S.tkw[lane];
+      }
+      if (first) P.active[a] = e;
+      if (lane == 0) *P.n_active = na;
+      for (int eb = 0; eb <= E; eb += kWave) {
+        const int ee = eb + lane;
+        int c = 0;
+        for (int j = 0; j < TK; ++j) c += S.tki[j] < ee;
+        if (ee <= E) P.offsets[ee] = c;
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // All threads of the workgroup.  Reads S.tki / S.tkw, writes S.off / S.slot /
-// S.act / S.misc[0]; `debug` also writes the plain copies to global memory.
+// S.act / S.misc[0] and the work model; `debug` also writes the plain copies
+// to global memory.
 __device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool debug) {
+  if (P.T * P.k <= kWave) {
+    build_perm_wave(P, S, debug);
+    return;
+  }
   const int tid = threadIdx.x;
   const int W = (P.T + 63) / 64;
   const int E = P.E, TK = P.T * P.k;
@@ -795,12 +887,11 @@ __device__ __forceinline__ int grab(int* ctr) {
 
 // Each workgroup owns a contiguous range of the n_active*F row pairs (equal
 // shares of the modelled work per workgroup); its waves take the row pairs one
-// at a time from an LDS counter (S.misc[1], set by set_counters), so the two
+// at a time from an LDS counter (S.misc[1], set by set_ranges), so the two
 // waves that share a SIMD, which issue at different rates, finish together.
 // A wave loads its next row pair while computing the current one.
 __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  int Q0, Q1;
-  work_range(S.cgu, uni(S.misc[0]), P.F, wg, G, Q0, Q1);
+  const int Q1 = uni(S.misc[3]);
   int* ctr = S.misc + 1;
   int r0 = grab(ctr);
   if (r0 >= Q1) return;
@@ -1005,8 +1096,7 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
 // current one.  An expert's tokens are taken two at a time, so W_down is read
 // once per two tokens.
 __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  int U0, U1;
-  work_range(S.cdn, uni(S.misc[0]), P.d / kDnRows, wg, G, U0, U1);
+  const int U1 = uni(S.misc[4]);
   int* ctr = S.misc + 2;
   float h[2][1][32];
   int ha = -1, hb = -1;
@@ -1034,16 +1124,26 @@ __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, ui
   return down_waves_static<MM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
 }
 
-// Workgroup work counters of the expert steps: the first row pair / down unit
-// of the workgroup's range.  All threads; ends with a barrier.
-__device__ __forceinline__ void set_counters(const Params& P, const Smem& S, int wg, int G) {
-  if (threadIdx.x == 0) {
+// The workgroup's ranges of the expert steps (equal shares of the modelled
+// work), computed once by wave 0: S.misc[1] / [2] = gate/up and down work
+// counters (starting at the first row pair / unit), [3] / [4] = range ends,
+// [5] / [6] = range starts.  Units: small-batch path, gate/up row pairs and
+// kDnRows-row down units; MFMA path, 128-row-pair and 512-row units.  All
+// threads; ends with a barrier.
+__device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int wg, int G) {
+  const int wave = threadIdx.x / kWave;
+  if (wave < 4) {  // waves 0-3: gate/up start and end, down start and end
     const int na = S.misc[0];
-    int q0, q1;
-    work_range(S.cgu, na, P.F, wg, G, q0, q1);
-    S.misc[1] = q0;
-    work_range(S.cdn, na, P.d / kDnRows, wg, G, q0, q1);
-    S.misc[2] = q0;
+    const bool gu = wave < 2;
+    const int R = gu ? (P.mfma ? (P.F + kGUUnitRows - 1) / kGUUnitRows : P.F)
+                     : (P.mfma ? (P.d + kDnUnitRows - 1) / kDnUnitRows : P.d / kDnRows);
+    const int v = row_at(gu ? S.cgu : S.cdn, na, R, wg + (wave & 1), G);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      if (wave == 0) S.misc[1] = S.misc[5] = v;
+      if (wave == 1) S.misc[3] = v;
+      if (wave == 2) S.misc[2] = S.misc[6] = v;
+      if (wave == 3) S.misc[4] = v;
+    }
   }
   __syncthreads();
 }
@@ -1257,8 +1357,7 @@ __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint
 __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int R = (P.F + kGUUnitRows - 1) / kGUUnitRows;
   const int nst = (P.d + kGUK * kKB - 1) / (kGUK * kKB);
-  int U0, U1;
-  work_range(S.cgu, uni(S.misc[0]), R, wg, G, U0, U1);
+  const int U0 = uni(S.misc[5]), U1 = uni(S.misc[3]);
   const int npos = seg_count(S, U0, U1, R, nst, kGUPass);
   if (npos == 0) return;
   char* t0 = reinterpret_cast<char*>(S.xs);
@@ -1463,8 +1562,7 @@ __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint
 __device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int R = (P.d + kDnUnitRows - 1) / kDnUnitRows;
   const int nst = (P.F + kDnK * kKB - 1) / (kDnK * kKB);
-  int U0, U1;
-  work_range(S.cdn, uni(S.misc[0]), R, wg, G, U0, U1);
+  const int U0 = uni(S.misc[6]), U1 = uni(S.misc[4]);
   const int npos = seg_count(S, U0, U1, R, nst, kDnPass);
   if (npos == 0) return;
   constexpr int kHalf = kDnK * kDnPass * kTileRow;
@@ -1558,7 +1656,7 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   stamp(P, wg, 2);
   if (s_ok) {
     build_perm(P, S, wg == 0);
-    set_counters(P, S, wg, G);
+    set_ranges(P, S, wg, G);
     stamp(P, wg, 3);
     bool dn = true;
     if (SMALL) {
@@ -1611,10 +1709,10 @@ __global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
   __syncthreads();
   if (!s_ok) return;
   build_perm(P, S, false);
+  set_ranges(P, S, blockIdx.x, gridDim.x);
   if (SMALL) {
     stage_x(P, S.xs, P.T, [](int r) { return r; });
     __syncthreads();
-    set_counters(P, S, blockIdx.x, gridDim.x);
     gate_up_waves(P, S, tag, blockIdx.x, gridDim.x);
   } else {
     gate_up_mfma(P, S, tag, blockIdx.x, gridDim.x);
@@ -1633,7 +1731,7 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   __syncthreads();
   if (!s_ok) return;
   build_perm(P, S, false);
-  set_counters(P, S, blockIdx.x, gridDim.x);
+  set_ranges(P, S, blockIdx.x, gridDim.x);
   if (MM == 0)
     down_mfma(P, S, tag, blockIdx.x, gridDim.x);
   else
