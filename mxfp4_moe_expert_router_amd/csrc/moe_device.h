@@ -198,25 +198,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return u2f(a) + u2f(b);
 }
 
+// Maximum of an unsigned 32-bit value over the 64 lanes; every lane gets it.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u<0x140>(v));  // row_mirror
+  uint32_t a, b;
+  swap16(v, a, b);
+  v = max(a, b);
+  swap32(v, a, b);
+  return max(a, b);
+}
+
 // Maximum of a 64-bit key over the 64 lanes; every lane receives it.
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t k) {
-  const uint64_t o = ((uint64_t)dpp_u<CTRL>((uint32_t)(k >> 32)) << 32) | dpp_u<CTRL>((uint32_t)k);
-  return max_u64(k, o);
-}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  k = dpp_max_u64<0xB1>(k);
-  k = dpp_max_u64<0x4E>(k);
-  k = dpp_max_u64<0x141>(k);
-  k = dpp_max_u64<0x140>(k);
-  uint32_t hl, hh, ll, lh;
-  swap16((uint32_t)(k >> 32), hl, hh);
-  swap16((uint32_t)k, ll, lh);
-  k = max_u64(((uint64_t)hl << 32) | ll, ((uint64_t)hh << 32) | lh);
-  swap32((uint32_t)(k >> 32), hl, hh);
-  swap32((uint32_t)k, ll, lh);
-  return max_u64(((uint64_t)hl << 32) | ll, ((uint64_t)hh << 32) | lh);
+  // high words first, then the low words of the lanes holding the top high
+  // word (a key with a zero low word never wins a tie, which callers avoid)
+  const uint32_t hi = wave_max_u32((uint32_t)(k >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(k >> 32) == hi ? (uint32_t)k : 0u);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Eight per-lane partial sums v[0..7] -> every lane receives the wave-wide

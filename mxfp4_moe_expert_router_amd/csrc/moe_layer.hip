@@ -348,8 +348,9 @@ __device__ __forceinline__ void router_step(const Params& P, const Smem& S, uint
 // ([P3-FP4] top-k routing).  Lane j < k returns expert j and gate j.
 // Returns false if the wait was abandoned.  Lane L holds the logits of
 // experts 2(L + 64m) + b in v[2m + b] (one 16-byte load per pair).
+// VPL: logits per lane (E <= 64 * VPL).
+template <int VPL>
 __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t, int* out_i, float* out_w, bool debug) {
-  constexpr int VPL = kMaxE / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t want = tag + P.withhold;
   const int E2 = (P.E + 1) & ~1, np = E2 / 2;
@@ -376,7 +377,7 @@ __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t,
       }
     }
     if (__all(ok)) break;
-    if (!keep_waiting(P, tag, t0, kSiteLogits, t, round, 2)) return false;
+    if (!keep_waiting(P, tag, t0, kSiteLogits, t, round, 0)) return false;  // few waves poll: short sleeps
   }
   if (debug) {
 #pragma unroll
@@ -395,16 +396,25 @@ __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t,
     const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
     key[i] = e < P.E ? ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e : 0ull;
   }
-  uint64_t mine = 0, top = 0;
+  // each lane keeps its largest remaining key; a round takes the wave maximum
+  // and only the lane that held it (keys are distinct) looks for its next one
+  uint64_t lb = 0, mine = 0, top = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (kWave * (i / 2) < np) lb = max_u64(lb, key[i]);  // uniform guard
   for (int j = 0; j < P.k; ++j) {
-    uint64_t best = 0;
+    const uint64_t best = wave_max_u64(lb);
+    if (lb == best) {
+      uint64_t nb = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (kWave * (i / 2) < np) best = max_u64(best, key[i]);  // uniform guard
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (key[i] == best) key[i] = 0ull;  // keys are distinct: one lane drops it
+      for (int i = 0; i < VPL; ++i) {
+        if (kWave * (i / 2) < np) {
+          if (key[i] == best) key[i] = 0ull;
+          nb = max_u64(nb, key[i]);
+        }
+      }
+      lb = nb;
+    }
     if (j == 0) top = best;
     if (lane == j) mine = best;
   }
@@ -435,7 +445,9 @@ __device__ __forceinline__ bool topk_publish(const Params& P, uint32_t tag, int 
   for (; t < T; t += NW) {
     int ii;
     float ww;
-    if (!topk_token(P, tag, t, &ii, &ww, true)) return false;
+    const bool ok = P.E <= 4 * kWave ? topk_token<4>(P, tag, t, &ii, &ww, true)
+                                     : topk_token<kMaxE / kWave>(P, tag, t, &ii, &ww, true);
+    if (!ok) return false;
     if (lane < P.k) {
       const uint32_t wb = __builtin_bit_cast(uint32_t, ww);
 #pragma unroll
@@ -471,7 +483,7 @@ __device__ __forceinline__ bool load_topk(const Params& P, const Smem& S, uint32
         }
       }
       if (__all(ready)) break;
-      if (!keep_waiting(P, tag, t0, kSiteTopk, base, round, 2)) {
+      if (!keep_waiting(P, tag, t0, kSiteTopk, base, round, 1)) {
         ok = false;
         break;
       }
@@ -1638,16 +1650,12 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   const uint32_t tag = start_call(P, wg, true);
   stamp(P, wg, 0);
   if (threadIdx.x == 0) s_ok = 1;
-  if (SMALL)
-    router_step<true>(P, S, tag, wg, G, [&] {
-      stage_x(P, S.xs, P.T, [](int r) { return r; });
-      __syncthreads();
-    });
-  else
-    router_step<false>(P, S, tag, wg, G, [] {});
+  router_step<false>(P, S, tag, wg, G, [] {});
   stamp(P, wg, 1);
   bool ok = topk_publish(P, tag, gw, NW);
   stamp(P, wg, 7);
+  // x into LDS while the top-k results are on their way (owner waves first)
+  if (SMALL) stage_x(P, S.xs, P.T, [](int r) { return r; });
   __syncthreads();
   ok = load_topk(P, S, tag, wg % kTopkRep) && ok;
   __syncthreads();
