@@ -323,6 +323,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t ld_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
 }
+// The same through this XCD's L2 (no cache-policy bits): several times
+// faster under full load, but the L2 may hold the line from an earlier call
+// (the words then carry an old tag).  Used for first attempts after
+// invalidate_l2; a word whose tag matches is exact either way, since each
+// tagged word is written once per call.
+__device__ __forceinline__ u32x4_t ld_cached16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Drops this XCD's L2 lines (and the CU's vector cache), so that later cached
+// reads of the workspace fetch what the other XCDs wrote through to memory.
+// Issued without a wait: later waits of the wave cover it.
+__device__ __forceinline__ void invalidate_l2() { __asm__ __volatile__("buffer_inv sc1" ::: "memory"); }
+
 __device__ __forceinline__ float tag_f32(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
 __device__ __forceinline__ int tag_i32(uint64_t w) { return (int)(uint32_t)w; }
 

@@ -76,6 +76,7 @@ constexpr int kMaxGrid = 2048;
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
 constexpr int kTraceSlots = 16;        // wall-clock stamps per workgroup (trace option)
 constexpr int kTopkRep = 8;            // copies of the top-k results (each read by 1/8 of the grid)
+constexpr int kRounds = 8;             // work rounds of the small-batch gate/up step (see set_ranges)
 // MFMA expert path (x does not fit in LDS)
 constexpr int kKB = 128;               // K elements per block
 constexpr int kDnTiles = 4;            // W_down tiles (16 rows) per wave
@@ -165,8 +166,13 @@ struct Smem {
   int* act;
   int* cgu;   // [n_active + 1] cumulative gate/up work per row, over active experts
   int* cdn;   // [n_active + 1] same for down
-  int* misc;  // [0] n_active, [8..8+kWaves) scan scratch
+  int* misc;  // [0] n_active, [1] / [2] work counters, [8..8+kWaves) scan scratch, [16..) round tables
 };
+
+// Round table of the small-batch expert steps (phase 0 gate/up, 1 down) in
+// S.misc: kRounds chunk starts, then kRounds + 1 cumulative chunk lengths.
+constexpr int kRoundTab = 2 * kRounds + 1;
+__device__ __forceinline__ int* round_tab(const Smem& S, int phase) { return S.misc + 16 + phase * kRoundTab; }
 
 __device__ __forceinline__ Smem carve(char* base, const Params& P, bool small) {
   const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small);
@@ -897,30 +903,60 @@ __device__ __forceinline__ int grab(int* ctr) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Each workgroup owns a contiguous range of the n_active*F row pairs (equal
-// shares of the modelled work per workgroup); its waves take the row pairs one
-// at a time from an LDS counter (S.misc[1], set by set_ranges), so the two
-// waves that share a SIMD, which issue at different rates, finish together.
-// A wave loads its next row pair while computing the current one.
+// A wave's walk through its workgroup's chunks (set_ranges): work index j of
+// the workgroup (from its LDS counter) is row unit start[k] + j - cum[k] of the
+// chunk k with cum[k] <= j < cum[k + 1].  A wave's indices only grow, so the
+// chunk only moves forward.
+struct Cursor {
+  int k, lo, hi, s;
+};
+__device__ __forceinline__ Cursor cursor_start(const int* tab) {
+  return Cursor{0, 0, uni(tab[kRounds + 1]), uni(tab[0])};
+}
+__device__ __forceinline__ int unit_of(const int* tab, Cursor& c, int j) {
+  while (j >= c.hi && c.k < kRounds - 1) {
+    ++c.k;
+    c.lo = c.hi;
+    c.hi = uni(tab[kRounds + c.k + 1]);
+    c.s = uni(tab[c.k]);
+  }
+  return c.s + (j - c.lo);
+}
+
+// Each workgroup owns kRounds chunks of the n_active*F row pairs (equal
+// shares of the modelled work); its waves take the row pairs one at a time
+// from an LDS counter (S.misc[1]), so the two waves that share a SIMD, which
+// issue at different rates, finish together.  A wave loads its next row pair
+// while computing the current one.
 __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  const int Q1 = uni(S.misc[3]);
+  const int* tab = round_tab(S, 0);
+  const int Q1 = uni(tab[2 * kRounds]);
   int* ctr = S.misc + 1;
-  int r0 = grab(ctr);
-  if (r0 >= Q1) return;
+  Cursor cur = cursor_start(tab);
+  // Each index is taken one step before its loads are issued, so the LDS
+  // atomic's round trip overlaps a compute step; indices only grow, so once
+  // one is past the end all later ones are too.
+  int j0 = grab(ctr);
+  if (j0 >= Q1) return;
+  int r0 = unit_of(tab, cur, j0);
   GURow A, B;
   gu_load(P, S, r0, A);
+  int j1 = grab(ctr);
   for (;;) {
-    // past the end of the range a wave re-reads the row pair it just loaded
-    // (cache-hot) and does not use it
-    const int r1 = grab(ctr);
-    gu_load(P, S, r1 < Q1 ? r1 : r0, B);
+    // past the end a wave re-reads the row pair it just loaded (cache-hot)
+    // and does not use it
+    const int r1 = j1 < Q1 ? unit_of(tab, cur, j1) : r0;
+    gu_load(P, S, r1, B);
+    const int j2 = grab(ctr);
     gu_compute_resident(P, S, tag, r0, A);
-    if (r1 >= Q1) break;
-    const int r2 = grab(ctr);
-    gu_load(P, S, r2 < Q1 ? r2 : r1, A);
+    if (j1 >= Q1) break;
+    const int r2 = j2 < Q1 ? unit_of(tab, cur, j2) : r1;
+    gu_load(P, S, r2, A);
+    const int j3 = grab(ctr);
     gu_compute_resident(P, S, tag, r1, B);
-    if (r2 >= Q1) break;
+    if (j2 >= Q1) break;
     r0 = r2;
+    j1 = j3;
   }
 }
 
@@ -963,27 +999,35 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq + (size_t)p * P.F, (uint32_t)P.F * 8u);
   const uint64_t t0 = wall_clock64();
   int round = 0;
-  // cheap pre-check first: two words per lane spread over the F rows (512 B
-  // per wave per round instead of the whole 8*F bytes)
+  // The first attempt reads the whole h at once and through the L2 (it is
+  // usually complete by then, and under full load every round trip costs
+  // microseconds, an agent-coherent one several times more); later attempts
+  // are coherent and first check two words per lane spread over the F rows
+  // (512 B per wave per round instead of the whole 8*F bytes).
+  const auto read_all = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const int c = lane + kWave * m;
+      const uint32_t base = (uint32_t)min(c, NCH - 1) * 256u;  // 32 tagged words per chunk
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const u32x4_t w = round == 0 ? ld_cached16(rs, base + v * 16u) : ld_coherent16(rs, base + v * 16u);
+        ok &= (w.y == tag) && (w.w == tag);
+        h[m][2 * v] = c < NCH ? u2f(w.x) : 0.f;
+        h[m][2 * v + 1] = c < NCH ? u2f(w.z) : 0.f;
+      }
+    }
+    return __all(ok);
+  };
   const uint32_t probe = (uint32_t)min((lane * P.F / kWave) & ~1, P.F - 2) * 8u;
   for (;;) {
-    const u32x4_t q = ld_coherent16(rs, probe);
-    if (__all((q.y == tag) && (q.w == tag))) {
-      bool ok = true;
-#pragma unroll
-      for (int m = 0; m < MM; ++m) {
-        const int c = lane + kWave * m;
-        const uint32_t base = (uint32_t)min(c, NCH - 1) * 256u;  // 32 tagged words per chunk
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const u32x4_t w = ld_coherent16(rs, base + v * 16u);
-          ok &= (w.y == tag) && (w.w == tag);
-          h[m][2 * v] = c < NCH ? u2f(w.x) : 0.f;
-          h[m][2 * v + 1] = c < NCH ? u2f(w.z) : 0.f;
-        }
-      }
-      if (__all(ok)) return true;
+    bool go = true;
+    if (round > 0) {  // uniform
+      const u32x4_t q = ld_coherent16(rs, probe);
+      go = __all((q.y == tag) && (q.w == tag));
     }
+    if (go && read_all()) return true;
     if (!keep_waiting(P, tag, t0, kSiteH, p, round, 3)) return false;
   }
 }
@@ -1102,30 +1146,37 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
   return true;
 }
 
-// F <= 2048: each workgroup owns a contiguous range of the down units (equal
-// shares of the modelled work per workgroup); its waves take units from an
-// LDS counter (S.misc[2]) and load the next unit's rows while computing the
-// current one.  An expert's tokens are taken two at a time, so W_down is read
-// once per two tokens.
+// F <= 2048: each workgroup owns kRounds chunks of the down units (equal
+// shares of the modelled work); its waves take units from an LDS counter
+// (S.misc[2]) and load the next unit's rows while computing the current one.
+// An expert's tokens are taken two at a time, so W_down is read once per two
+// tokens.
 __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  const int U1 = uni(S.misc[4]);
+  const int* tab = round_tab(S, 1);
+  const int U1 = uni(tab[2 * kRounds]);
   int* ctr = S.misc + 2;
+  Cursor cur = cursor_start(tab);
   float h[2][1][32];
   int ha = -1, hb = -1;
-  int u0 = grab(ctr);
-  if (u0 >= U1) return true;
+  int j0 = grab(ctr);
+  if (j0 >= U1) return true;
+  int u0 = unit_of(tab, cur, j0);
   DnRows<1, kDnRows> A, B;
   dn_unit_rows(P, S, u0, A);
+  int j1 = grab(ctr);  // indices are taken one step ahead (see gate_up_waves)
   for (;;) {
-    const int u1 = grab(ctr);
-    dn_unit_rows(P, S, u1 < U1 ? u1 : u0, B);  // past the end: re-read (cache-hot), unused
+    const int u1 = j1 < U1 ? unit_of(tab, cur, j1) : u0;  // past the end: re-read (cache-hot), unused
+    dn_unit_rows(P, S, u1, B);
+    const int j2 = grab(ctr);
     if (!dn_unit_work(P, S, tag, u0, A, h, ha, hb)) return false;
-    if (u1 >= U1) break;
-    const int u2 = grab(ctr);
-    dn_unit_rows(P, S, u2 < U1 ? u2 : u1, A);
+    if (j1 >= U1) break;
+    const int u2 = j2 < U1 ? unit_of(tab, cur, j2) : u1;
+    dn_unit_rows(P, S, u2, A);
+    const int j3 = grab(ctr);
     if (!dn_unit_work(P, S, tag, u1, B, h, ha, hb)) return false;
-    if (u2 >= U1) break;
+    if (j2 >= U1) break;
     u0 = u2;
+    j1 = j3;
   }
   return true;
 }
@@ -1136,26 +1187,69 @@ __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, ui
   return down_waves_static<MM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
 }
 
-// The workgroup's ranges of the expert steps (equal shares of the modelled
-// work), computed once by wave 0: S.misc[1] / [2] = gate/up and down work
-// counters (starting at the first row pair / unit), [3] / [4] = range ends,
-// [5] / [6] = range starts.  Units: small-batch path, gate/up row pairs and
-// kDnRows-row down units; MFMA path, 128-row-pair and 512-row units.  All
-// threads; ends with a barrier.
+// The workgroup's share of the expert steps.  Work units: small-batch path,
+// gate/up row pairs and kDnRows-row down units; MFMA path, 128-row-pair and
+// 512-row units.  Both lists are expert-major over the active experts.
+//  - Small-batch path: the gate/up list is cut into kRounds * G chunks of
+//    equal modelled work, and workgroup wg owns chunks k * G + wg, k <
+//    kRounds, so all workgroups move through the experts together and the h
+//    of all but the last round's experts is complete well before the gate/up
+//    step ends; the down list is cut into G contiguous ranges (one chunk per
+//    workgroup, so a wave rarely needs a new h).  Work tables in round_tab;
+//    S.misc[1] / [2] = 0: gate/up and down counters over the workgroup's
+//    chunks.
+//  - MFMA path: one contiguous range per list: S.misc[5] / [3] = gate/up start
+//    and end (S.misc[1] its counter), S.misc[6] / [4] = down start and end
+//    (S.misc[2]).
+// All threads; ends with a barrier.
 __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int wg, int G) {
-  const int wave = threadIdx.x / kWave;
-  if (wave < 4) {  // waves 0-3: gate/up start and end, down start and end
-    const int na = S.misc[0];
-    const bool gu = wave < 2;
-    const int R = gu ? (P.mfma ? (P.F + kGUUnitRows - 1) / kGUUnitRows : P.F)
-                     : (P.mfma ? (P.d + kDnUnitRows - 1) / kDnUnitRows : P.d / kDnRows);
-    const int v = row_at(gu ? S.cgu : S.cdn, na, R, wg + (wave & 1), G);
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-      if (wave == 0) S.misc[1] = S.misc[5] = v;
-      if (wave == 1) S.misc[3] = v;
-      if (wave == 2) S.misc[2] = S.misc[6] = v;
-      if (wave == 3) S.misc[4] = v;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int na = S.misc[0];
+  if (P.mfma) {
+    if (wave < 4) {  // waves 0-3: gate/up start and end, down start and end
+      const bool gu = wave < 2;
+      const int R = gu ? (P.F + kGUUnitRows - 1) / kGUUnitRows : (P.d + kDnUnitRows - 1) / kDnUnitRows;
+      const int v = row_at(gu ? S.cgu : S.cdn, na, R, wg + (wave & 1), G);
+      if (lane == 0) {
+        if (wave == 0) S.misc[1] = S.misc[5] = v;
+        if (wave == 1) S.misc[3] = v;
+        if (wave == 2) S.misc[2] = S.misc[6] = v;
+        if (wave == 3) S.misc[4] = v;
+      }
     }
+    __syncthreads();
+    return;
+  }
+  // waves 0-3: the gate/up chunk boundaries, b = 2k + side of chunk k (side 0
+  // its start, 1 its end); waves 4-7: the two down chunks' boundaries
+  if (wave < 4) {
+    int* tab = round_tab(S, 0);
+    for (int b = wave; b < 2 * kRounds; b += 4) {
+      const int k = b >> 1, side = b & 1;
+      const int v = row_at(S.cgu, na, P.F, k * G + wg + side, kRounds * G);
+      if (lane == 0) tab[side ? kRounds + k : k] = v;  // ends parked where the lengths go
+    }
+  } else if (wave < 6) {
+    int* tab = round_tab(S, 1);
+    const int side = wave & 1;
+    const int v = row_at(S.cdn, na, P.d / kDnRows, wg + side, G);
+    if (lane == 0) {
+      tab[side ? kRounds : 0] = v;
+      if (wave == 4)
+        for (int c = 1; c < kRounds; ++c) tab[c] = tab[kRounds + c] = 0;  // empty chunks
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    int* t = round_tab(S, threadIdx.x);
+    int run = 0;
+    for (int k = 0; k < kRounds; ++k) {
+      const int len = t[kRounds + k] - t[k];
+      t[kRounds + k] = run;
+      run += len;
+    }
+    t[2 * kRounds] = run;
+    S.misc[1 + threadIdx.x] = 0;
   }
   __syncthreads();
 }
@@ -1433,6 +1527,7 @@ __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int 
 // kHRow, word pair = piece % kHRow).
 constexpr int kHRow = kDnK * kKB / 2;  // word pairs per pair row of a step
 constexpr int kHPieces = kDnPass * kHRow / kWG;
+template <bool COHERENT>
 __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
                                               u32x4_t (&v)[kHPieces]) {
   const int np = max(1, min(kDnPass, c.ne - c.pass));
@@ -1440,7 +1535,8 @@ __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __a
   for (int m = 0; m < kHPieces; ++m) {
     const int pc = (int)threadIdx.x + kWG * m;
     const int n = min(pc / kHRow, np - 1), k = min(c.j * kDnK * kKB + 2 * (pc % kHRow), P.F - 2);
-    v[m] = ld_coherent16(rs, ((uint32_t)(c.p0 + c.pass + n) * (uint32_t)P.F + (uint32_t)k) * 8u);
+    const uint32_t off = ((uint32_t)(c.p0 + c.pass + n) * (uint32_t)P.F + (uint32_t)k) * 8u;
+    v[m] = COHERENT ? ld_coherent16(rs, off) : ld_cached16(rs, off);
   }
 }
 
@@ -1467,7 +1563,7 @@ __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __
     int round = 0;
     for (;;) {
       if (!keep_waiting(P, tag, t0, kSiteH, c.p0 + c.pass, round, 3)) break;
-      dn_mfma_hload(P, c, rs, v);
+      dn_mfma_hload<true>(P, c, rs, v);
       if (__all(current())) break;
     }
   }
@@ -1557,7 +1653,7 @@ __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint
                                             f32x4_t (&acc)[kDnTiles][2]) {
   constexpr int kHalf = kDnK * kDnPass * kTileRow;  // hi tile; lo tile follows
   u32x4_t hr[kHPieces];
-  dn_mfma_hload(P, nc, rs, hr);  // first: waiting for it below must not wait for An
+  dn_mfma_hload<false>(P, nc, rs, hr);  // first: waiting for it below must not wait for An
   dn_mfma_load(P, nc, R, An);
   if (cc.ne - cc.pass > 16)
     dn_mfma_step<2>(Ac, cur, cur + kHalf, acc);
@@ -1590,7 +1686,7 @@ __device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32
   for (int t = 0; t < kDnTiles; ++t) acc[t][0] = acc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
     u32x4_t hr[kHPieces];
-    dn_mfma_hload(P, nc, rs, hr);
+    dn_mfma_hload<false>(P, nc, rs, hr);
     dn_mfma_load(P, nc, R, A0);
     dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf);
     seg_next(S, U1, R, nst, kDnPass, nc);
@@ -1667,6 +1763,12 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
     set_ranges(P, S, wg, G);
     stamp(P, wg, 3);
     bool dn = true;
+    // Before the down step's cached first reads of h, the L2 of every XCD
+    // drops its lines of earlier calls: one wave of workgroups 0-7 (one per
+    // XCD, as workgroups are dealt to the XCDs in turn; were it otherwise, a
+    // stale line only sends its readers to the coherent path).  Its own
+    // gate/up loads wait for it, the other waves' do not.
+    if (wg < 8 && threadIdx.x >= kWG - kWave) invalidate_l2();
     if (SMALL) {
       gate_up_waves(P, S, tag, wg, G);
       stamp(P, wg, 4);
@@ -1740,6 +1842,7 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   if (!s_ok) return;
   build_perm(P, S, false);
   set_ranges(P, S, blockIdx.x, gridDim.x);
+  if (threadIdx.x < kWave) invalidate_l2();  // before the cached first reads of h
   if (MM == 0)
     down_mfma(P, S, tag, blockIdx.x, gridDim.x);
   else
