@@ -55,7 +55,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU clocks take some tens of ms of load to ramp up")
     ap.add_argument("--workload", default="verify",
                     choices=["tiny", "decode", "verify", "batched_verify", "dense"])
     ap.add_argument("--replicas", type=int, default=4, help="distinct copies of the expert weights")

@@ -856,7 +856,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
   const int a = uni(rho / P.F), i = uni(rho % P.F);
   const int e = uni(S.act[a]);
   const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
-  for (int tb = 0; tb < ne; tb += kGUTok) {
+  const auto group = [&](int tb) {
     const int nb = min(kGUTok, ne - tb);
     float g[kGUTok], u[kGUTok];
     int xrow[kGUTok];
@@ -893,7 +893,12 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
           st_tagged(&P.hq[(size_t)(p0 + tb + t) * P.F + i], __builtin_bit_cast(uint32_t, swiglu(gs, us)), tag);
       }
     }
-  }
+  };
+  // The first group (usually the only one) outside any loop: a loop whose
+  // body reads the row pair's registers makes the compiler wait for every
+  // load in flight (vmcnt(0)) at its entry, including the next row pair's.
+  group(0);
+  for (int tb = kGUTok; tb < ne; tb += kGUTok) group(tb);
 }
 
 // Next unit from a workgroup's LDS work counter (one LDS atomic by lane 0).
