@@ -58,7 +58,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first: the GPU clocks take some tens of ms of load to ramp up")
     ap.add_argument("--workload", default="verify",
-                    choices=["tiny", "decode", "verify", "batched_verify", "dense"])
+                    choices=["tiny", "decode", "verify", "batched_verify", "dense",
+                             "sweep_T4", "sweep_T16", "sweep_T22", "sweep_T32"])
     ap.add_argument("--replicas", type=int, default=4, help="distinct copies of the expert weights")
     ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")

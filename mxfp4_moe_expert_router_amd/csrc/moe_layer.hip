@@ -117,6 +117,8 @@ struct Params {
   uint64_t spin_ticks;
   uint32_t withhold;  // test knob: top-k waits for a tag the router never writes
   int mfma;           // 1: x does not fit in LDS, expert steps on MFMA
+  int xmode;          // small-batch path: 0 x of every token in LDS, 1 x of the workgroup's pairs (see stage_pairs)
+  int xrows;          // small-batch path: rows of x the LDS holds
 };
 
 // ------------------------------------------------------------ LDS layout ----
@@ -127,15 +129,17 @@ struct LdsPlan {
 
 __host__ __device__ inline size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-__host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, bool small) {
+// xrows > 0: the small-batch path with that many rows of x in LDS; 0: the
+// MFMA path.
+__host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, int xrows) {
   LdsPlan L;
   const size_t TK = (size_t)T * k;
   const size_t W = ((size_t)T + 63) / 64;
   const size_t mask_bytes = (size_t)E * W * 8;
   size_t o = 0;
-  if (small) {
-    // x of all tokens stays resident; the permutation masks get their own space
-    L.xs = o; o = al16(o + (size_t)T * d * 2);
+  if (xrows > 0) {
+    // rows of x stay resident; the permutation masks get their own space
+    L.xs = o; o = al16(o + (size_t)xrows * d * 2);
     L.mask = o; o = al16(o + mask_bytes);
   } else {
     // the activation tiles of the MFMA path are used after the permutation is
@@ -166,16 +170,18 @@ struct Smem {
   int* act;
   int* cgu;   // [n_active + 1] cumulative gate/up work per row, over active experts
   int* cdn;   // [n_active + 1] same for down
-  int* misc;  // [0] n_active, [1] / [2] work counters, [8..8+kWaves) scan scratch, [16..) round tables
+  int* misc;  // [0] n_active, [1] / [2] work counters, [8..8+kWaves) scan scratch, [16..50) round tables,
+              // [50] / [51] staged x rows (xmode 1)
 };
 
 // Round table of the small-batch expert steps (phase 0 gate/up, 1 down) in
 // S.misc: kRounds chunk starts, then kRounds + 1 cumulative chunk lengths.
 constexpr int kRoundTab = 2 * kRounds + 1;
+constexpr int kMiscXBase = 50, kMiscXRows = 51;  // x rows staged in LDS (xmode 1): first pair, count
 __device__ __forceinline__ int* round_tab(const Smem& S, int phase) { return S.misc + 16 + phase * kRoundTab; }
 
 __device__ __forceinline__ Smem carve(char* base, const Params& P, bool small) {
-  const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small);
+  const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, small ? P.xrows : 0);
   Smem S;
   S.xs = reinterpret_cast<u32x4_t*>(base + L.xs);
   S.mask = reinterpret_cast<uint64_t*>(base + L.mask);
@@ -847,8 +853,12 @@ __device__ __forceinline__ void gu_dot(const Params& P, const u32x4_t* xs, int x
 
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
-// Small batches: x of every token resident in LDS (row t = token t).  Each
-// chunk of the row pair is decoded once and used for up to kGUTok tokens.
+// Small batches: x in LDS (xmode 0: row t = token t; xmode 1: row r = pair
+// xbase + r, see stage_pairs).  Each chunk of the row pair is decoded once and
+// used for up to kGUTok tokens.  A token group whose pairs are not in LDS
+// (xmode 1, more pairs in the workgroup's range than LDS rows) reads x from
+// global memory instead: correct, slower.
+template <bool XP>
 __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem& S, uint32_t tag, int rho,
                                                     const GURow& R) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -856,14 +866,17 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
   const int a = uni(rho / P.F), i = uni(rho % P.F);
   const int e = uni(S.act[a]);
   const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
-  const auto group = [&](int tb) {
+  const int xb0 = XP ? uni(S.misc[kMiscXBase]) : 0, xn = XP ? uni(S.misc[kMiscXRows]) : 0;
+  const auto group = [&](int tb, auto global_x) {
+    constexpr bool GX = decltype(global_x)::value;
     const int nb = min(kGUTok, ne - tb);
     float g[kGUTok], u[kGUTok];
     int xrow[kGUTok];
 #pragma unroll
     for (int t = 0; t < kGUTok; ++t) {
       g[t] = u[t] = 0.f;
-      xrow[t] = t < nb ? uni(S.slot[p0 + tb + t]) / P.k : 0;
+      const int pr = p0 + tb + t;
+      xrow[t] = t < nb ? (GX || !XP ? uni(S.slot[pr]) / P.k : pr - xb0) : 0;
     }
 #pragma unroll
     for (int m = 0; m < kGUChunks; ++m) {
@@ -875,10 +888,16 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
 #pragma unroll
         for (int t = 0; t < kGUTok; ++t) {
           if (t < nb) {
-            const u32x4_t* xb = S.xs + (size_t)xrow[t] * 4 * NCH;
             u32x4_t xq[4];
+            if (GX) {
+              const u32x4_t* xg = reinterpret_cast<const u32x4_t*>(P.x + (size_t)xrow[t] * P.d) + 4 * cc;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + cc];
+              for (int q = 0; q < 4; ++q) xq[q] = xg[q];
+            } else {
+              const u32x4_t* xb = S.xs + (size_t)xrow[t] * 4 * NCH;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + cc];
+            }
             g[t] = dot32_bf16_dec(dg, xq, g[t]);
             u[t] = dot32_bf16_dec(du, xq, u[t]);
           }
@@ -894,11 +913,39 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
       }
     }
   };
+  const auto run = [&](int tb) {
+    const int nb = min(kGUTok, ne - tb);
+    if (!XP || (p0 + tb >= xb0 && p0 + tb + nb <= xb0 + xn))  // uniform
+      group(tb, std::false_type{});
+    else
+      group(tb, std::true_type{});
+  };
   // The first group (usually the only one) outside any loop: a loop whose
   // body reads the row pair's registers makes the compiler wait for every
   // load in flight (vmcnt(0)) at its entry, including the next row pair's.
-  group(0);
-  for (int tb = kGUTok; tb < ne; tb += kGUTok) group(tb);
+  run(0);
+  for (int tb = kGUTok; tb < ne; tb += kGUTok) run(tb);
+}
+
+// xmode 1: x rows of the pairs of the experts the workgroup's gate/up range
+// touches, as many as the LDS holds (row r = pair xbase + r), into
+// S.misc[kMiscXBase] / [kMiscXRows].  After set_ranges (one chunk); all
+// threads; ends with a barrier.
+__device__ __forceinline__ void stage_pairs(const Params& P, const Smem& S) {
+  const int* tab = round_tab(S, 0);
+  const int q0 = tab[0], q1 = q0 + tab[kRounds + 1];
+  int pb = 0, n = 0;
+  if (q1 > q0) {
+    const int a0 = q0 / P.F, a1 = (q1 - 1) / P.F;
+    pb = S.off[S.act[a0]];
+    n = min(S.off[S.act[a1] + 1] - pb, P.xrows);
+  }
+  if (threadIdx.x == 0) {
+    S.misc[kMiscXBase] = pb;
+    S.misc[kMiscXRows] = n;
+  }
+  if (n > 0) stage_x(P, S.xs, n, [&](int r) { return S.slot[pb + r] / P.k; });
+  __syncthreads();
 }
 
 // Next unit from a workgroup's LDS work counter (one LDS atomic by lane 0).
@@ -933,6 +980,8 @@ __device__ __forceinline__ int unit_of(const int* tab, Cursor& c, int j) {
 // from an LDS counter (S.misc[1]), so the two waves that share a SIMD, which
 // issue at different rates, finish together.  A wave loads its next row pair
 // while computing the current one.
+// XP: x rows of the workgroup's pairs in LDS (stage_pairs); else all tokens'.
+template <bool XP>
 __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int* tab = round_tab(S, 0);
   const int Q1 = uni(tab[2 * kRounds]);
@@ -953,12 +1002,12 @@ __device__ __forceinline__ void gate_up_waves(const Params& P, const Smem& S, ui
     const int r1 = j1 < Q1 ? unit_of(tab, cur, j1) : r0;
     gu_load(P, S, r1, B);
     const int j2 = grab(ctr);
-    gu_compute_resident(P, S, tag, r0, A);
+    gu_compute_resident<XP>(P, S, tag, r0, A);
     if (j1 >= Q1) break;
     const int r2 = j2 < Q1 ? unit_of(tab, cur, j2) : r1;
     gu_load(P, S, r2, A);
     const int j3 = grab(ctr);
-    gu_compute_resident(P, S, tag, r1, B);
+    gu_compute_resident<XP>(P, S, tag, r1, B);
     if (j2 >= Q1) break;
     r0 = r2;
     j1 = j3;
@@ -1130,14 +1179,43 @@ __device__ __forceinline__ void dn_unit_rows(const Params& P, const Smem& S, int
 
 // One unit against every token of its expert, two tokens per pass; the h of
 // the pass is kept in registers across units of the same expert.
+// HL: h rows staged in LDS by stage_h (row r = pair hb0 + r), read for every
+// pass (kept in registers across units it costs more registers than the
+// wave has); else each wave loads the h it needs from global memory and keeps
+// it across the units of the same expert and token pair.
+template <bool HL>
 __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uint32_t tag, int u,
-                                             const DnRows<1, kDnRows>& R, float (&h)[2][1][32], int& ha, int& hb) {
+                                             const DnRows<1, kDnRows>& R, float (&h)[2][1][32], int& ha, int& hb,
+                                             int hb0) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int upe = P.d / kDnRows;
   const int a = uni(u / upe), e = uni(S.act[a]);
   const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
   const int r = (u - a * upe) * kDnRows;
   for (int tg = 0; tg < ne; tg += 2) {
     const int nt = min(2, ne - tg);
+    if (HL) {
+      // lanes past the row's chunks read the last chunk's h: their codes have
+      // scale 0 (dn_load), so it contributes 0
+      float hl[2][1][32];
+      const int c = min(lane, P.F / 32 - 1);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int pr = p0 + tg + min(tt, nt - 1);
+        const f32x4_t* hp =
+            reinterpret_cast<const f32x4_t*>(S.xs) + ((size_t)(pr - hb0) * P.F + (size_t)c * 32) / 4;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const f32x4_t q = hp[v];
+          hl[tt][0][4 * v] = q.x;
+          hl[tt][0][4 * v + 1] = q.y;
+          hl[tt][0][4 * v + 2] = q.z;
+          hl[tt][0][4 * v + 3] = q.w;
+        }
+      }
+      dn_compute<1, 2, kDnRows>(P, S, tag, p0 + tg, nt, r, kDnRows, R, hl);
+      continue;
+    }
     if (ha != a || hb != tg) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -1151,12 +1229,77 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
   return true;
 }
 
-// F <= 2048: each workgroup owns kRounds chunks of the down units (equal
-// shares of the modelled work); its waves take units from an LDS counter
-// (S.misc[2]) and load the next unit's rows while computing the current one.
-// An expert's tokens are taken two at a time, so W_down is read once per two
-// tokens.
-__device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+// The h of the pairs of the experts the workgroup's down range touches, read
+// once by the whole workgroup into LDS (S.xs as floats, row r = pair hb0 + r)
+// when they fit in cap_bytes and it pays; the waves then take each pass's h
+// from LDS instead of each loading it (coherent 16-byte loads of a ready h
+// cost several microseconds under full load, and an expert with more than two
+// tokens needs a new h for every pass).  Every wave takes the same decision
+// from the LDS tables: `staged` and hb0 out.  When staging, all threads: the
+// first barrier orders every wave's last read of x in S.xs before the writes
+// of h; ends with a barrier.  False: the wait timed out.
+__device__ __forceinline__ bool stage_h(const Params& P, const Smem& S, uint32_t tag, size_t cap_bytes, bool& staged,
+                                        int& hb0) {
+  __shared__ int s_bad[2], s_go;
+  const int* tab = round_tab(S, 1);
+  const int q0 = uni(tab[0]), q1 = q0 + uni(tab[kRounds + 1]);
+  const int upe = P.d / kDnRows;
+  int pb = 0, np = 0, many = 0;
+  if (q1 > q0) {
+    const int a0 = q0 / upe, a1 = (q1 - 1) / upe;
+    pb = uni(S.off[S.act[a0]]);
+    np = uni(S.off[S.act[a1] + 1]) - pb;
+    for (int a = a0; a <= a1 && !many; ++a) many = S.off[S.act[a] + 1] - S.off[S.act[a]] > 2;
+  }
+  // Staging costs a workgroup barrier and puts the h latency before the
+  // first weight loads; it pays where waves would reload h per pass (an expert
+  // with more than two tokens) or have few units to spread their own h loads
+  // over (fewer than 8 per wave).
+  const bool worth = __builtin_amdgcn_readfirstlane(many) || q1 - q0 < 8 * kWaves;
+  staged = worth && np > 0 && (size_t)np * P.F * 4 <= cap_bytes;
+  hb0 = pb;
+  if (!staged) return true;
+  if (threadIdx.x == 0) s_bad[0] = 0;
+  __syncthreads();
+  float* hl = reinterpret_cast<float*>(S.xs);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq + (size_t)pb * P.F, (uint32_t)np * (uint32_t)P.F * 8u);
+  const int n16 = np * P.F / 2;  // 16-byte pieces of two tagged words
+  const uint64_t t0 = wall_clock64();
+  for (int round = 0;;) {
+    const int par = round & 1;
+    if (threadIdx.x == 0) s_bad[par ^ 1] = 0;  // the next round's flag
+    bool ok = true;
+    for (int i = threadIdx.x; i < n16; i += kWG) {
+      // first read through the L2 (dropped of earlier calls' lines, see k_layer)
+      const u32x4_t w = round == 0 ? ld_cached16(rs, (uint32_t)i * 16u) : ld_coherent16(rs, (uint32_t)i * 16u);
+      if (w.y == tag && w.w == tag) {
+        hl[2 * i] = u2f(w.x);
+        hl[2 * i + 1] = u2f(w.z);
+      } else {
+        ok = false;
+      }
+    }
+    if (!ok) s_bad[par] = 1;
+    __syncthreads();
+    if (s_bad[par] == 0) return true;  // uniform
+    if (threadIdx.x < kWave) {
+      int rd = round;
+      const bool go = keep_waiting(P, tag, t0, kSiteH, pb, rd, 3);
+      if (threadIdx.x == 0) s_go = go ? 1 : 0;
+    }
+    ++round;
+    __syncthreads();
+    if (!s_go) return false;
+  }
+}
+
+// F <= 2048: each workgroup owns a range of the down units (equal shares of
+// the modelled work); its waves take units from an LDS counter (S.misc[2])
+// and load the next unit's rows while computing the current one.  An
+// expert's tokens are taken two at a time, so W_down is read once per two
+// tokens.  HL: h from LDS (stage_h).
+template <bool HL>
+__device__ __forceinline__ bool down_loop(const Params& P, const Smem& S, uint32_t tag, int hb0) {
   const int* tab = round_tab(S, 1);
   const int U1 = uni(tab[2 * kRounds]);
   int* ctr = S.misc + 2;
@@ -1173,12 +1316,12 @@ __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, u
     const int u1 = j1 < U1 ? unit_of(tab, cur, j1) : u0;  // past the end: re-read (cache-hot), unused
     dn_unit_rows(P, S, u1, B);
     const int j2 = grab(ctr);
-    if (!dn_unit_work(P, S, tag, u0, A, h, ha, hb)) return false;
+    if (!dn_unit_work<HL>(P, S, tag, u0, A, h, ha, hb, hb0)) return false;
     if (j1 >= U1) break;
     const int u2 = j2 < U1 ? unit_of(tab, cur, j2) : u1;
     dn_unit_rows(P, S, u2, A);
     const int j3 = grab(ctr);
-    if (!dn_unit_work(P, S, tag, u1, B, h, ha, hb)) return false;
+    if (!dn_unit_work<HL>(P, S, tag, u1, B, h, ha, hb, hb0)) return false;
     if (j2 >= U1) break;
     u0 = u2;
     j1 = j3;
@@ -1186,9 +1329,23 @@ __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, u
   return true;
 }
 
-template <int MM>
-__device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
-  if (MM == 1) return down_waves_dyn(P, S, tag, wg, G);
+// HS: the workgroup may stage h in LDS (stage_h; all threads, x_bytes = the x
+// area it may use); else every wave loads its own h.
+template <bool HS>
+__device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, size_t x_bytes) {
+  if (!HS) return down_loop<false>(P, S, tag, 0);
+  bool staged;
+  int hb0;
+  if (!stage_h(P, S, tag, x_bytes, staged, hb0)) return false;
+  if (staged) return down_loop<true>(P, S, tag, hb0);  // uniform
+  return down_loop<false>(P, S, tag, hb0);
+}
+
+
+template <int MM, bool HS>
+__device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int wg, int G,
+                                              size_t x_bytes) {
+  if (MM == 1) return down_waves_dyn<HS>(P, S, tag, x_bytes);
   return down_waves_static<MM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
 }
 
@@ -1229,11 +1386,14 @@ __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int w
   // its start, 1 its end); waves 4-7: the two down chunks' boundaries
   if (wave < 4) {
     int* tab = round_tab(S, 0);
-    for (int b = wave; b < 2 * kRounds; b += 4) {
+    const int nr = P.xmode ? 1 : kRounds;  // xmode 1: one range (its pairs' x is staged)
+    for (int b = wave; b < 2 * nr; b += 4) {
       const int k = b >> 1, side = b & 1;
-      const int v = row_at(S.cgu, na, P.F, k * G + wg + side, kRounds * G);
+      const int v = row_at(S.cgu, na, P.F, k * G + wg + side, nr * G);
       if (lane == 0) tab[side ? kRounds + k : k] = v;  // ends parked where the lengths go
     }
+    if (wave == 0 && lane == 0)
+      for (int c = nr; c < kRounds; ++c) tab[c] = tab[kRounds + c] = 0;  // empty chunks
   } else if (wave < 6) {
     int* tab = round_tab(S, 1);
     const int side = wave & 1;
@@ -1739,10 +1899,17 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
 
 // ---------------------------------------------------------- kernels ---------
 
-// The whole layer in one launch.  SMALL: x of all tokens resident in LDS and
-// top-k published once per token.  MM: W_down chunks per lane.
-template <bool SMALL, int MM>
+// Expert-step variants of the whole-layer kernel (the host picks one, see
+// plan_launch): kVAll, x of every token in LDS; kVAllH, the same with the down
+// step's h staged per workgroup (stage_h, for few units per workgroup);
+// kVPairs, x of each workgroup's own pairs in LDS and h staged; kVMfma, the
+// MFMA expert steps.
+constexpr int kVAll = 0, kVAllH = 1, kVPairs = 2, kVMfma = 3;
+
+// The whole layer in one launch.  V: variant; MM: W_down chunks per lane.
+template <int V, int MM>
 __global__ void __launch_bounds__(kWG) k_layer(Params P) {
+  constexpr bool SMALL = V != kVMfma, XP = V == kVPairs, HS = V == kVAllH || V == kVPairs;
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_ok;
   const Smem S = carve(smem, P, SMALL);
@@ -1756,7 +1923,7 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   bool ok = topk_publish(P, tag, gw, NW);
   stamp(P, wg, 7);
   // x into LDS while the top-k results are on their way (owner waves first)
-  if (SMALL) stage_x(P, S.xs, P.T, [](int r) { return r; });
+  if (SMALL && !XP) stage_x(P, S.xs, P.T, [](int r) { return r; });
   __syncthreads();
   ok = load_topk(P, S, tag, wg % kTopkRep) && ok;
   __syncthreads();
@@ -1766,6 +1933,7 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   if (s_ok) {
     build_perm(P, S, wg == 0);
     set_ranges(P, S, wg, G);
+    if (XP) stage_pairs(P, S);
     stamp(P, wg, 3);
     bool dn = true;
     // Before the down step's cached first reads of h, the L2 of every XCD
@@ -1775,10 +1943,10 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
     // gate/up loads wait for it, the other waves' do not.
     if (wg < 8 && threadIdx.x >= kWG - kWave) invalidate_l2();
     if (SMALL) {
-      gate_up_waves(P, S, tag, wg, G);
+      gate_up_waves<XP>(P, S, tag, wg, G);
       stamp(P, wg, 4);
       stamp_gu_wave(P, wg);
-      dn = down_dispatch<MM>(P, S, tag, wg, G);
+      dn = down_dispatch<MM, HS>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
     } else {
       gate_up_mfma(P, S, tag, wg, G);
       stamp(P, wg, 4);
@@ -1826,9 +1994,14 @@ __global__ void __launch_bounds__(kWG) k_st_gate_up(Params P) {
   build_perm(P, S, false);
   set_ranges(P, S, blockIdx.x, gridDim.x);
   if (SMALL) {
-    stage_x(P, S.xs, P.T, [](int r) { return r; });
-    __syncthreads();
-    gate_up_waves(P, S, tag, blockIdx.x, gridDim.x);
+    if (P.xmode == 0) {
+      stage_x(P, S.xs, P.T, [](int r) { return r; });
+      __syncthreads();
+      gate_up_waves<false>(P, S, tag, blockIdx.x, gridDim.x);
+    } else {
+      stage_pairs(P, S);
+      gate_up_waves<true>(P, S, tag, blockIdx.x, gridDim.x);
+    }
   } else {
     gate_up_mfma(P, S, tag, blockIdx.x, gridDim.x);
   }
@@ -1848,10 +2021,13 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   build_perm(P, S, false);
   set_ranges(P, S, blockIdx.x, gridDim.x);
   if (threadIdx.x < kWave) invalidate_l2();  // before the cached first reads of h
-  if (MM == 0)
+  if (MM == 0) {
     down_mfma(P, S, tag, blockIdx.x, gridDim.x);
-  else
-    down_dispatch<MM == 0 ? 1 : MM>(P, S, tag, blockIdx.x, gridDim.x);
+  } else {
+    // the x area of this layout: the MFMA tiles or the masks, whichever is larger
+    const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, 0);
+    down_dispatch<MM == 0 ? 1 : MM, true>(P, S, tag, blockIdx.x, gridDim.x, L.tki - L.xs);
+  }
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
@@ -1912,8 +2088,11 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
 }
 
 // x of all tokens fits in LDS next to the permutation tables.
-static bool use_small(const moe_mxfp4_dims* dm, int32_t k) {
-  return lds_plan(dm->T, dm->d, dm->E, k, true).total <= (size_t)kLdsMax;
+// Rows of x the small-batch path's LDS can hold next to its tables.
+static int x_rows_fit(const moe_mxfp4_dims* dm, int32_t k) {
+  const size_t tables = lds_plan(dm->T, dm->d, dm->E, k, 1).total - al16((size_t)dm->d * 2);
+  if (tables >= (size_t)kLdsMax) return 0;
+  return (int)(((size_t)kLdsMax - tables) / ((size_t)dm->d * 2));
 }
 
 
@@ -1926,9 +2105,13 @@ struct DeviceInfo {
 static std::mutex g_mu;
 static DeviceInfo g_info[64];
 
-static const void* layer_kernel(bool small, int mm) {
-  if (small) return mm == 1 ? (const void*)k_layer<true, 1> : (const void*)k_layer<true, 2>;
-  return mm == 1 ? (const void*)k_layer<false, 1> : (const void*)k_layer<false, 2>;
+static const void* layer_kernel(int v, int mm) {
+  switch (v) {
+    case kVAll: return mm == 1 ? (const void*)k_layer<kVAll, 1> : (const void*)k_layer<kVAll, 2>;
+    case kVAllH: return (const void*)k_layer<kVAllH, 1>;  // the static down path (mm 2) stages nothing
+    case kVPairs: return mm == 1 ? (const void*)k_layer<kVPairs, 1> : (const void*)k_layer<kVPairs, 2>;
+    default: return mm == 1 ? (const void*)k_layer<kVMfma, 1> : (const void*)k_layer<kVMfma, 2>;
+  }
 }
 
 static int device_info(DeviceInfo* out) {
@@ -1940,7 +2123,9 @@ static int device_info(DeviceInfo* out) {
     int cus = 0, khz = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_EDEVICE;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_EDEVICE;
-    const void* ks[] = {layer_kernel(true, 1), layer_kernel(true, 2), layer_kernel(false, 1), layer_kernel(false, 2),
+    const void* ks[] = {layer_kernel(kVAll, 1), layer_kernel(kVAll, 2), layer_kernel(kVAllH, 1),
+                        layer_kernel(kVPairs, 1), layer_kernel(kVPairs, 2), layer_kernel(kVMfma, 1),
+                        layer_kernel(kVMfma, 2),
                         (const void*)k_st_perm, (const void*)k_st_gate_up<true>, (const void*)k_st_gate_up<false>,
                         (const void*)k_st_down<0>, (const void*)k_st_down<1>, (const void*)k_st_down<2>};
     for (const void* f : ks) {
@@ -1998,6 +2183,8 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.spin_ticks = us * di.ticks_per_us;
   P.withhold = 0;
   P.mfma = 0;
+  P.xmode = 0;
+  P.xrows = 0;
   return P;
 }
 
@@ -2020,16 +2207,44 @@ struct Launch {
   bool small;
   int mm;
   size_t lds;
+  int xmode, xrows;
+  int v;  // kernel variant
 };
 
+// Expert-step path: x of every token in LDS (small-batch VALU path, xmode 0);
+// else, up to kPairMaxT tokens, the x rows of each workgroup's own pairs
+// (xmode 1: a few experts per workgroup, about T*k/n_active tokens each);
+// else the MFMA path.
+constexpr int kPairMaxT = 48;
 static int plan_launch(const moe_mxfp4_dims* dm, int32_t k, Launch* L) {
-  L->small = use_small(dm, k);
+  const int fit = x_rows_fit(dm, k);
+  L->small = true;
+  L->xmode = 0;
+  L->xrows = dm->T;
+  if (fit < dm->T) {
+    if (dm->T <= kPairMaxT && fit >= 4) {
+      L->xmode = 1;
+      L->xrows = fit;
+    } else {
+      L->small = false;
+      L->xrows = 0;
+    }
+  }
   L->mm = chunks_per_lane_down(dm);
   if (L->mm < 1 || L->mm > 2) return MOE_ESHAPE;
-  const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->small);
+  // one or two tokens: few down units per workgroup, the h is best staged once
+  // per workgroup (kVAllH)
+  L->v = !L->small ? kVMfma : L->xmode == 1 ? kVPairs : (dm->T <= 2 && L->mm == 1) ? kVAllH : kVAll;
+  const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->xrows);
   if (pl.total > (size_t)kLdsMax) return MOE_ESHAPE;
   L->lds = pl.total;
   return MOE_OK;
+}
+
+static void apply_launch(Params& P, const Launch& L) {
+  P.mfma = L.small ? 0 : 1;
+  P.xmode = L.xmode;
+  P.xrows = L.xrows;
 }
 
 // The layer's waits need every workgroup resident at once.  The grid is at
@@ -2042,9 +2257,9 @@ static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s, bool
   void* args[] = {&P};
   hipError_t e;
   if (cooperative)
-    e = hipLaunchCooperativeKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
+    e = hipLaunchCooperativeKernel(layer_kernel(L.v, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
   else
-    e = hipLaunchKernel(layer_kernel(L.small, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
+    e = hipLaunchKernel(layer_kernel(L.v, L.mm), dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return MOE_ELAUNCH;
@@ -2053,7 +2268,7 @@ static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s, bool
 }
 
 static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t s, bool experts) {
-  const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, false).total;
+  const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, 0).total;
   hipLaunchKernelGGL(k_st_router, dim3(grid), dim3(kWG), 0, s, P);
   hipLaunchKernelGGL(k_st_topk, dim3(grid), dim3(kWG), 0, s, P);
   if (experts) {
@@ -2136,7 +2351,7 @@ int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk) {
   DeviceInfo di;
   st = device_info(&di);
   if (st != MOE_OK) return -st;
-  return grid_for(di, layer_kernel(L.small, L.mm), L.lds, 0);
+  return grid_for(di, layer_kernel(L.v, L.mm), L.lds, 0);
 }
 
 int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
@@ -2158,11 +2373,11 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
   if (st != MOE_OK) return st;
   Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di,
                          opts ? opts->spin_limit_us : 0u);
-  P.mfma = L.small ? 0 : 1;
+  apply_launch(P, L);
   if (opts && (opts->flags & MOE_OPT_WITHHOLD_ARRIVAL)) P.withhold = 1;
   if (opts && (opts->flags & MOE_OPT_TRACE))
     P.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + make_layout(dims, topk).trace);
-  const int grid = grid_for(di, layer_kernel(L.small, L.mm), L.lds, opts ? opts->grid : 0);
+  const int grid = grid_for(di, layer_kernel(L.v, L.mm), L.lds, opts ? opts->grid : 0);
   return launch_layer(P, L, grid, (hipStream_t)stream, opts && (opts->flags & MOE_OPT_COOPERATIVE));
 }
 
@@ -2189,7 +2404,7 @@ int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const fl
   st = device_info(&di);
   if (st != MOE_OK) return st;
   Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di, 0u);
-  P.mfma = L.small ? 0 : 1;
+  apply_launch(P, L);
   return launch_staged(P, L, di.cus, (hipStream_t)stream, true);
 }
 
@@ -2210,7 +2425,7 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
   if (st != MOE_OK) return st;
   // packed/scales/out are not touched by the routing kernels
   Params P = make_params(dims, topk, x, router_w, nullptr, nullptr, nullptr, workspace, di, 0u);
-  P.mfma = L.small ? 0 : 1;
+  apply_launch(P, L);
   hipStream_t s = (hipStream_t)stream;
   st = launch_staged(P, L, di.cus, s, false);
   if (st != MOE_OK) return st;

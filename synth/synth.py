@@ -55,13 +55,18 @@ class Config:
         return replace(self, T=T, name=f"{self.name}_T{T}")
 
 
-# The five workloads of the layer (sizes from the task's workload list).
+# The five workloads of the layer, and the verify-block sizes of the sweep.
 _BASE = {
     "tiny": Config("tiny", T=8, d=256, F=128, E=8, k=2),
     "decode": Config("decode", T=1, d=7168, F=2048, E=256, k=8),
     "verify": Config("verify", T=8, d=7168, F=2048, E=256, k=8),
     "batched_verify": Config("batched_verify", T=128, d=7168, F=2048, E=256, k=8, zipf_s=1.1),
     "dense": Config("dense", T=512, d=7168, F=2048, E=256, k=8),
+    # verify-block size sweep (uniform routing, same shapes as verify)
+    "sweep_T4": Config("sweep_T4", T=4, d=7168, F=2048, E=256, k=8),
+    "sweep_T16": Config("sweep_T16", T=16, d=7168, F=2048, E=256, k=8),
+    "sweep_T22": Config("sweep_T22", T=22, d=7168, F=2048, E=256, k=8),
+    "sweep_T32": Config("sweep_T32", T=32, d=7168, F=2048, E=256, k=8),
 }
 
 

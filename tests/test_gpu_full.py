@@ -5,7 +5,8 @@ single launch with its default grid).
 decode (T=1) and verify (T=8): every output element against the oracle.
 batched_verify (T=128, Zipf-skewed routing) and dense (T=512): routing and
 permutation for all tokens, outputs for a sample of tokens (the oracle runs
-only those tokens' expert pairs).
+only those tokens' expert pairs).  The verify-block sweep (T = 4, 16, 22, 32)
+likewise, sampled from T = 22 on.
 """
 import numpy as np
 import pytest
@@ -83,3 +84,19 @@ def test_batched_verify_T128_zipf(full_env):
 
 def test_dense_T512(full_env):
     _run(full_env, "dense", sample=[0, 1, 255, 256, 300, 511])
+
+
+def test_sweep_T4(full_env):
+    _run(full_env, "sweep_T4")
+
+
+def test_sweep_T16(full_env):
+    _run(full_env, "sweep_T16")
+
+
+def test_sweep_T22(full_env):
+    _run(full_env, "sweep_T22", sample=[0, 7, 8, 15, 21])
+
+
+def test_sweep_T32(full_env):
+    _run(full_env, "sweep_T32", sample=[0, 9, 16, 30, 31])

@@ -79,7 +79,8 @@ SMALL = [
     dict(T=64, d=1056, F=224, E=4, k=2),       # ~32 tokens per expert: many LDS token passes
     dict(T=33, d=2080, F=2080, E=64, k=8),     # 65 chunks per row: second lane pass of one chunk
     dict(T=5, d=7168, F=2048, E=12, k=3),      # full-width experts, few of them
-    dict(T=40, d=4096, F=128, E=6, k=2),       # x too large for LDS: MFMA expert path
+    dict(T=40, d=4096, F=128, E=6, k=2),       # x too large for LDS: each workgroup stages its pairs' rows
+    dict(T=48, d=7168, F=64, E=4, k=2),        # ~24 tokens per expert, 10 LDS rows: staged and global x groups
     dict(T=100, d=2048, F=2080, E=16, k=4),    # MFMA path, F % 128 != 0
     dict(T=96, d=1024, F=256, E=4, k=2),       # MFMA path: ~48 tokens per expert, two token passes
     dict(T=100, d=800, F=96, E=3, k=2),        # MFMA path: partial K blocks and partial row units
