@@ -90,6 +90,12 @@ __device__ __forceinline__ float dot32_bf16_dec(const bf16x2_t (&v)[16], const u
 // D (16 x 16, fp32): lane l holds column l % 16, rows 4(l / 16) .. +4.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+// D = A B + C on 16x16 fp32 tiles, K = 4 per instruction, fp32 products and
+// sums: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and holds
+// D[4 (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -65,6 +65,8 @@ constexpr int kWaves = kWG / kWave;    // waves per workgroup
 constexpr int kLdsMax = 160 * 1024 - 1024;  // dynamic LDS per workgroup (gfx950 has 160 KiB; static LDS needs a few bytes)
 constexpr int kRouterTok = 8;          // tokens per router unit
 constexpr int kRouterF4 = 4;           // float4 per lane of a router unit's wave (d / 8 <= 1024 columns)
+constexpr int kRouterTileBytes = 8 * 16 * 16 * 4;  // router_mfma: one 16 x 16 fp32 tile per wave
+constexpr int kRouterMfmaT = 64;       // router_mfma above this many tokens (router_step up to it)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxD = 8192;
@@ -124,7 +126,7 @@ struct Params {
 // ------------------------------------------------------------ LDS layout ----
 // Shared by host (size) and device (carving).
 struct LdsPlan {
-  size_t xs, mask, tki, tkw, off, slot, act, cgu, cdn, misc, total;
+  size_t xs, mask, tki, tkw, off, slot, act, cgu, cdn, misc, rt, total;
 };
 
 __host__ __device__ inline size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -156,6 +158,7 @@ __host__ __device__ inline LdsPlan lds_plan(int T, int d, int E, int k, int xrow
   L.cgu = o; o = al16(o + ((size_t)E + 1) * 4);
   L.cdn = o; o = al16(o + ((size_t)E + 1) * 4);
   L.misc = o; o = al16(o + 64 * 4);
+  L.rt = o; o = al16(o + (T > kRouterMfmaT ? kRouterTileBytes : 0));  // router_mfma's partial tiles
   L.total = o;
   return L;
 }
@@ -170,6 +173,7 @@ struct Smem {
   int* act;
   int* cgu;   // [n_active + 1] cumulative gate/up work per row, over active experts
   int* cdn;   // [n_active + 1] same for down
+  float* rt;  // router_mfma's partial tiles (more than kRouterMfmaT tokens)
   int* misc;  // [0] n_active, [1] / [2] work counters, [8..8+kWaves) scan scratch, [16..50) round tables,
               // [50] / [51] staged x rows (xmode 1)
 };
@@ -193,6 +197,7 @@ __device__ __forceinline__ Smem carve(char* base, const Params& P, bool small) {
   S.cgu = reinterpret_cast<int*>(base + L.cgu);
   S.cdn = reinterpret_cast<int*>(base + L.cdn);
   S.misc = reinterpret_cast<int*>(base + L.misc);
+  S.rt = reinterpret_cast<float*>(base + L.rt);
   return S;
 }
 
@@ -291,6 +296,86 @@ __device__ __forceinline__ void stamp_gu_wave(const Params& P, int wg) {
 // see stage_x), else from global memory.  `pre` (all threads) runs once, after
 // the first unit's weight loads are issued: it overlaps the x staging with
 // them.  All threads of the workgroup.
+// Router for more than kRouterMfmaT tokens ([P1-FP4] higher-precision
+// router): logits = x W_r^T in fp32 on v_mfma_f32_16x16x4_f32, so that W_r
+// and x are read once per 16 x 16 tile instead of once per (expert, 8 tokens)
+// (T=512: 58 us instead of 200).  A unit moves ~0.7 MB at one CU's share of
+// the bandwidth (~30 us), so for fewer tokens, with fewer units than CUs,
+// router_step's finer units finish first.  Unit =
+// (16 experts, 16 tokens), one workgroup; wave w sums K blocks of 16
+// [w nkb / 8, (w + 1) nkb / 8).  In K block j, lane l loads 4 consecutive K
+// (16j + 4 (l / 16) .. +3) of expert row l % 16 and of token row l % 16, and
+// MFMA step s uses element s of both (each step sums a permuted but matching
+// set of 4 K).  The 8 partial tiles are added in wave order; a lane past the
+// last expert or token reads a clamped row and its result is not stored.
+// tile: kRouterTileBytes of LDS.
+__device__ __forceinline__ void router_mfma(const Params& P, uint32_t tag, int wg, int G, float* tile) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int ne16 = (P.E + 15) / 16, nt16 = (P.T + 15) / 16;
+  const int nkb = P.d / 16;
+  const int kb0 = wave * nkb / kWaves, kb1 = (wave + 1) * nkb / kWaves;
+  const int E2 = (P.E + 1) & ~1;
+  const int r = lane & 15, q = lane >> 4;
+  for (int u = wg; u < ne16 * nt16; u += G) {
+    const int e0 = (u / nt16) * 16, t0 = (u % nt16) * 16;
+    const f32x4_t* w = reinterpret_cast<const f32x4_t*>(P.wr + (size_t)min(e0 + r, P.E - 1) * P.d) + q;
+    const uint2* xr = reinterpret_cast<const uint2*>(P.x + (size_t)min(t0 + r, P.T - 1) * P.d) + q;
+    // K blocks in groups of kRB, the next group's loads in flight while the
+    // current one runs (blocks past kb1 re-read block kb1 - 1 and are skipped)
+    // four accumulators (one per MFMA step), so that consecutive MFMAs do not
+    // wait for each other's results; added at the end
+    constexpr int kRB = 8;
+    f32x4_t acc4[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) acc4[s4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t a[2][kRB];
+    uint2 b[2][kRB];
+    const auto load = [&](int g, int j0) {
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        const int j = min(j0 + i, kb1 - 1);
+        a[g][i] = w[4 * j];
+        b[g][i] = xr[4 * j];
+      }
+    };
+    const auto run = [&](int g, int j0) {
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        if (j0 + i < kb1) {  // uniform
+          acc4[0] = mfma_f32(a[g][i].x, bf16lo(b[g][i].x), acc4[0]);
+          acc4[1] = mfma_f32(a[g][i].y, bf16hi(b[g][i].x), acc4[1]);
+          acc4[2] = mfma_f32(a[g][i].z, bf16lo(b[g][i].y), acc4[2]);
+          acc4[3] = mfma_f32(a[g][i].w, bf16hi(b[g][i].y), acc4[3]);
+        }
+      }
+    };
+    if (kb1 > kb0) {
+      load(0, kb0);
+      for (int j = kb0; j < kb1; j += 2 * kRB) {
+        load(1, j + kRB);
+        run(0, j);
+        if (j + kRB >= kb1) break;
+        load(0, j + 2 * kRB);
+        run(1, j + kRB);
+      }
+    }
+    const f32x4_t acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    // D row = expert 4q + i, column = token r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[wave * 256 + (4 * q + i) * 16 + r] = acc[i];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int ei = threadIdx.x >> 4, ti = threadIdx.x & 15;
+      float l = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) l += tile[v * 256 + ei * 16 + ti];
+      if (e0 + ei < P.E && t0 + ti < P.T)
+        st_tagged(&P.lgp[(size_t)(t0 + ti) * E2 + e0 + ei], __builtin_bit_cast(uint32_t, l), tag);
+    }
+    __syncthreads();
+  }
+}
+
 template <bool XLDS, class Pre>
 __device__ __forceinline__ void router_step(const Params& P, const Smem& S, uint32_t tag, int wg, int G, Pre pre) {
   __shared__ float s_part[kWaves][kRouterTok];
@@ -1918,7 +2003,10 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
   const uint32_t tag = start_call(P, wg, true);
   stamp(P, wg, 0);
   if (threadIdx.x == 0) s_ok = 1;
-  router_step<false>(P, S, tag, wg, G, [] {});
+  if (P.T > kRouterMfmaT)
+    router_mfma(P, tag, wg, G, S.rt);
+  else
+    router_step<false>(P, S, tag, wg, G, [] {});
   stamp(P, wg, 1);
   bool ok = topk_publish(P, tag, gw, NW);
   stamp(P, wg, 7);
@@ -1962,8 +2050,12 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
 
 // One launch per step (the per-operator model), same arithmetic.
 __global__ void __launch_bounds__(kWG) k_st_router(Params P) {
+  extern __shared__ __align__(16) char smem[];  // kRouterTileBytes for more than kRouterMfmaT tokens
   const uint32_t tag = start_call(P, blockIdx.x, false);
-  router_step<false>(P, Smem{}, tag, blockIdx.x, gridDim.x, [] {});
+  if (P.T > kRouterMfmaT)
+    router_mfma(P, tag, blockIdx.x, gridDim.x, reinterpret_cast<float*>(smem));
+  else
+    router_step<false>(P, Smem{}, tag, blockIdx.x, gridDim.x, [] {});
 }
 __global__ void __launch_bounds__(kWG) k_st_topk(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
@@ -2269,7 +2361,7 @@ static int launch_layer(Params P, const Launch& L, int grid, hipStream_t s, bool
 
 static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t s, bool experts) {
   const unsigned lds_tables = (unsigned)lds_plan(P.T, P.d, P.E, P.k, 0).total;
-  hipLaunchKernelGGL(k_st_router, dim3(grid), dim3(kWG), 0, s, P);
+  hipLaunchKernelGGL(k_st_router, dim3(grid), dim3(kWG), P.T > kRouterMfmaT ? kRouterTileBytes : 0, s, P);
   hipLaunchKernelGGL(k_st_topk, dim3(grid), dim3(kWG), 0, s, P);
   if (experts) {
     if (L.small)
