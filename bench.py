@@ -59,7 +59,7 @@ def main():
                     help="untimed steps first: the GPU clocks take some tens of ms of load to ramp up")
     ap.add_argument("--workload", default="verify",
                     choices=["tiny", "decode", "verify", "batched_verify", "dense",
-                             "sweep_T4", "sweep_T16", "sweep_T22", "sweep_T32"])
+                             "sweep_T4", "sweep_T16", "sweep_T22", "sweep_T32", "quantize"])
     ap.add_argument("--replicas", type=int, default=4, help="distinct copies of the expert weights")
     ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -77,6 +77,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+        return
+
+    if args.workload == "quantize":
+        if args.gpus != 1:
+            print(json.dumps({"error": "one GPU only", "n_gpus": args.gpus}))
+            sys.exit(2)
+        bench_quantize(args)
         return
 
     if args.gpus != 1:
@@ -222,6 +229,65 @@ def main():
             "sample": sample + f"; fp64 C oracle, {cpu_s:.2f} s wall, {nth} OpenMP threads",
             "us_per_layer": round(cpu_layer_s * 1e6, 1),
         }
+    print(json.dumps(result), flush=True)
+
+
+def bench_quantize(args):
+    """MXFP4 quantize/pack (moe_mxfp4_quantize) of 16 experts' worth of fp32
+    weights (16 x 3 x 2048 rows of 7168 values, N(0, 0.02)), device resident.
+    Algorithmic bytes: 4 per value read, 0.5 + 1/32 per value written."""
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_router_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows, K = 16 * 3 * 2048, 7168
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    w = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32).mul_(0.02)
+    packed = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        moe.quantize(w, packed, scales)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        moe.quantize(w, packed, scales)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    n = rows * K
+    alg = n * 4 + n // 2 + n // 32
+    kern_s = float(ms.mean()) * 1e-3
+    step_s = elapsed / args.steps
+    result = {
+        "metric": "achieved HBM GB/s (% of peak), MXFP4 quantize/pack of fp32 weights on the GPU",
+        "value": round(alg / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "dtype_detail": "fp32 in, E2M1 codes + E8M0 scales out, decisions in fp64", "data": "synthetic",
+        "config": {"workload": f"quantize: {rows} x {K} fp32 (16 experts of d=7168, ffn=2048)", "rows": rows, "K": K},
+        "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved": round(alg / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_quantize<false>", "kernel_us_mean": round(kern_s * 1e6, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        sr = 256  # a sample of rows, scaled per value
+        ws = w[:sr].double().cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.quantize(ws)
+        cpu_s = (time.perf_counter() - t1) * rows / sr
+        result["cpu_baseline"] = {"value": round(alg / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{sr} of {rows} rows, single-threaded C oracle, scaled per value"}
     print(json.dumps(result), flush=True)
 
 

@@ -216,6 +216,27 @@ const char* moe_mxfp4_strerror(int status);
  * sizes, or a negative moe_status. */
 int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
 
+/* ---- MXFP4 quantize / pack on the GPU ([P3-FP4] 4-bit values with a shared
+ * per-block scale; [MX] conversion): the direction opposite to the layer's
+ * decode, to prepare expert weights in the layout above on the device.
+ *
+ *   w       rows x K values, row-major, device; fp32 (dtype MOE_QDTYPE_F32) or
+ *           bf16 bit patterns (MOE_QDTYPE_BF16); 16-byte aligned; finite.
+ *   packed  rows x K/2 bytes (device, 4-byte aligned, overwritten): element c
+ *           of a row in byte c/2, low nibble for even c.
+ *   scales  rows x K/32 bytes (device, overwritten): the E8M0 byte of each
+ *           32-element block.
+ * Rule per block: X = floor(log2 max|v|) - 2 clamped to [-127, 127] (-127 for
+ * an all-zero block), scale byte X + 127; each element to the E2M1 magnitude
+ * nearest |v| / 2^X, ties to the even mantissa bit, saturating at 6; sign bit
+ * when v < 0.  Non-finite inputs give unspecified codes.
+ * Errors: MOE_EINVAL (null pointer, negative size, unknown dtype), MOE_ESHAPE
+ * (K not a multiple of 32), MOE_EALIGN, MOE_EDEVICE, MOE_ELAUNCH.  rows = 0 or
+ * K = 0 does nothing.  Enqueued on `stream`; nothing is allocated. */
+enum { MOE_QDTYPE_F32 = 0, MOE_QDTYPE_BF16 = 1 };
+int moe_mxfp4_quantize(const void* w, int32_t dtype, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ETIMEOUT, MOE_E
 MOE_OPT_WITHHOLD_ARRIVAL = 0x1
 MOE_OPT_TRACE = 0x2
 MOE_OPT_COOPERATIVE = 0x4
+MOE_QDTYPE_F32, MOE_QDTYPE_BF16 = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,8 @@ def _load():
     lib.moe_mxfp4_strerror.argtypes = [ctypes.c_int]
     lib.moe_mxfp4_persistent_grid.restype = ctypes.c_int
     lib.moe_mxfp4_persistent_grid.argtypes = [P(Dims), i32]
+    lib.moe_mxfp4_quantize.restype = ctypes.c_int
+    lib.moe_mxfp4_quantize.argtypes = [vp, i32, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
     return lib
 
 
@@ -251,3 +254,19 @@ def intermediates(workspace: torch.Tensor, dims: LayerDims, topk: int) -> dict:
         "y": tagged(lay.y, TK * d).view(TK, d),
         "trace": view(lay.trace, 2048 * 16, torch.int64).view(2048, 16),
     }
+
+
+def quantize(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+             stream=None):
+    """MXFP4 quantize/pack of a 2-D fp32 or bf16 device tensor [rows, K] on the GPU
+    (moe_mxfp4_quantize): returns (packed uint8 [rows, K/2], scales uint8 [rows, K/32])."""
+    if w.dim() != 2 or w.dtype not in (torch.float32, torch.bfloat16) or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D fp32 or bf16 CUDA tensor")
+    rows, K = w.shape
+    if packed is None:
+        packed = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=w.device)
+    dt = MOE_QDTYPE_F32 if w.dtype == torch.float32 else MOE_QDTYPE_BF16
+    _check(lib.moe_mxfp4_quantize(_ptr(w), dt, rows, K, _ptr(packed), _ptr(scales), _stream(stream)), "quantize")
+    return packed, scales

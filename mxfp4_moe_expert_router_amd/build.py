@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = [os.path.join(PKG, "csrc", "moe_layer.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "moe_layer.hip"), os.path.join(PKG, "csrc", "mxfp4_quant.hip")]
 HEADERS = [os.path.join(PKG, "csrc", "moe_device.h"), os.path.join(ROOT, "include", "moe_mxfp4.h")]
 
 HIPCC_FLAGS = [

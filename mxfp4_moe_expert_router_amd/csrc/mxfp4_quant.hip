@@ -1,0 +1,173 @@
+// MXFP4 quantize / pack on the GPU: rows of fp32 or bf16 weights -> E2M1 codes
+// (two per byte, even element in the low nibble) and one E8M0 scale byte per
+// 32-element block ([P3-FP4] 4-bit values sharing a per-block scale; [MX]
+// conversion), the direction opposite to the layer's decode, for preparing
+// expert weights on the device.
+//
+// Rule (one block of 32 values v): amax = max |v|; shared exponent
+// X = floor(log2 amax) - 2 (E2M1's largest exponent is 2), clamped to
+// [-127, 127], X = -127 when amax = 0; the scale byte is X + 127.  Each
+// element goes to the E2M1 magnitude nearest |v| / 2^X, a tie to the one with
+// an even mantissa bit, and above 6 to 6; the sign bit is set when v < 0.
+//
+// Layout of the work: a wave quantizes 16 blocks at a time, every load
+// instruction reading 1 KiB of contiguous input (see k_quantize); a block's
+// maximum comes from lane exchanges within its lane group.  Every decision is taken on the fp32 bit patterns
+// with integer operations: for values >= 0 the order of the patterns is the
+// order of the values (subnormals included), and each decision point
+// t 2^X (t = 0.25, 0.75, ..., 5: at most three significant bits) is an exact
+// fp32 value whose pattern is built with shifts, so the codes are exact and
+// do not depend on how the hardware treats subnormal arithmetic.  HBM-bound:
+// 4.5 bytes per element (fp32 in) or 2.5 (bf16 in).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mxfp4.h"
+
+namespace moe_q {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// fp32 bit pattern of m 2^p for a small odd integer m (1, 3, 5, 7) and
+// -149 <= p, p + floor(log2 m) <= 127.
+__device__ __forceinline__ uint32_t f32_bits_of(uint32_t m, int p) {
+  const int n = 31 - __builtin_clz(m);  // floor(log2 m)
+  const int ex = p + n + 127;
+  if (ex >= 1) return ((uint32_t)ex << 23) | ((m << (23 - n)) & 0x7FFFFFu);
+  return m << (p + 149);  // subnormal: m 2^p = (m 2^(p + 149)) 2^-149
+}
+
+// floor(log2 |v|) of a nonzero finite fp32 pattern without its sign bit.
+__device__ __forceinline__ int ilog2_bits(uint32_t a) {
+  const int ex = (int)(a >> 23);
+  if (ex > 0) return ex - 127;
+  return (31 - __builtin_clz(a)) - 149;  // subnormal
+}
+
+// The codes of one block from its elements' patterns: every lane of the
+// block's lane group holds N of them; the group (G lanes, aligned) exchanges
+// its maximum.  Returns the lane's N codes packed (element 0 in the low
+// nibble) and the block's X.
+template <int N, int G>
+__device__ __forceinline__ uint32_t block_codes(const uint32_t (&u)[N], int& Xout) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) amax = max(amax, u[i] & 0x7FFFFFFFu);
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+  const int X = amax ? min(max(ilog2_bits(amax) - 2, -127), 127) : -127;
+  // decision points t 2^X, t = 1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5; at a tie the
+  // even mantissa bit wins: strictly above for 1/4, 5/4, 5/2, 5 and at or
+  // above for 3/4, 7/4, 7/2
+  const uint32_t d0 = f32_bits_of(1, X - 2), d1 = f32_bits_of(3, X - 2), d2 = f32_bits_of(5, X - 2),
+                 d3 = f32_bits_of(7, X - 2), d4 = f32_bits_of(5, X - 1), d5 = f32_bits_of(7, X - 1),
+                 d6 = f32_bits_of(5, X);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t a = u[i] & 0x7FFFFFFFu;
+    const uint32_t code = (uint32_t)(a > d0) + (uint32_t)(a >= d1) + (uint32_t)(a > d2) + (uint32_t)(a >= d3) +
+                          (uint32_t)(a > d4) + (uint32_t)(a >= d5) + (uint32_t)(a > d6);
+    // sign bit for v < 0 (a negative zero keeps code 0 without it)
+    word |= (code | ((u[i] >> 31) && a ? 8u : 0u)) << (4 * i);
+  }
+  Xout = X;
+  return word;
+}
+
+// A wave takes 16 blocks at a time, kU chunks of them per round with all
+// the round's loads issued first.  fp32: two 1 KiB loads per chunk, lane l
+// holding elements 4l..4l+3 of each half (8 lanes per block); bf16: one 1 KiB
+// load, lane l holding elements 8l..8l+7 (4 lanes per block).  Every load
+// instruction reads 1 KiB of contiguous input; chunks past the end re-read
+// the last chunk (in bounds) and store nothing.
+constexpr int kU = 4;
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) k_quantize(const void* w, int64_t nblocks, uint8_t* packed,
+                                                       uint8_t* scales) {
+  constexpr int kH = BF16 ? 1 : 2;  // 1 KiB loads per chunk
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t nchunks = (nblocks + 15) / 16;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w);
+  for (int64_t c0 = wave; c0 < nchunks; c0 += kU * nwaves) {
+    u32x4_t r[kU][kH];
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int64_t c = min(c0 + q * nwaves, nchunks - 1);
+#pragma unroll
+      for (int hf = 0; hf < kH; ++hf) {
+        // the last chunk may be partial: its lanes past the end read a clamped piece
+        const int64_t piece = min(c * 64 * kH + hf * 64 + lane, nblocks * 4 * kH - 1);
+        r[q][hf] = src[piece];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int64_t c = c0 + q * nwaves;
+      if (c >= nchunks) break;  // uniform
+      if (BF16) {
+        const int64_t b = c * 16 + (lane >> 2);
+        uint32_t u[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t two = r[q][0][i];
+          u[2 * i] = two << 16;
+          u[2 * i + 1] = two & 0xFFFF0000u;
+        }
+        int X;
+        const uint32_t word = block_codes<8, 4>(u, X);  // the block's four lanes agree on b < nblocks
+        if (b < nblocks) {
+          reinterpret_cast<uint32_t*>(packed)[c * 64 + lane] = word;
+          if ((lane & 3) == 0) scales[b] = (uint8_t)(X + 127);
+        }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int64_t b = c * 16 + hf * 8 + (lane >> 3);
+          uint32_t u[4] = {r[q][hf][0], r[q][hf][1], r[q][hf][2], r[q][hf][3]};
+          int X;
+          const uint32_t word = block_codes<4, 8>(u, X);
+          if (b < nblocks) {
+            reinterpret_cast<uint16_t*>(packed)[c * 128 + hf * 64 + lane] = (uint16_t)word;
+            if ((lane & 7) == 0) scales[b] = (uint8_t)(X + 127);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe_q
+
+extern "C" int moe_mxfp4_quantize(const void* w, int32_t dtype, int64_t rows, int64_t K, uint8_t* packed,
+                                  uint8_t* scales, void* stream) {
+  if (rows < 0 || K < 0 || (dtype != MOE_QDTYPE_F32 && dtype != MOE_QDTYPE_BF16)) return MOE_EINVAL;
+  if (K % 32 != 0) return MOE_ESHAPE;
+  const int64_t nblocks = rows * (K / 32);
+  if (nblocks == 0) return MOE_OK;
+  if (!w || !packed || !scales) return MOE_EINVAL;
+  if ((uintptr_t)w % 16 || (uintptr_t)packed % 4) return MOE_EALIGN;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_EDEVICE;
+  }
+  // enough workgroups to fill the CUs several times over, at most one chunk of 16 blocks per wave
+  int64_t grid = ((nblocks + 15) / 16 + moe_q::kThreads / 64 - 1) / (moe_q::kThreads / 64);
+  const int64_t cap = (int64_t)cus * 16;
+  if (grid > cap) grid = cap;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == MOE_QDTYPE_BF16)
+    hipLaunchKernelGGL(moe_q::k_quantize<true>, dim3((unsigned)grid), dim3(moe_q::kThreads), 0, s, w, nblocks,
+                       packed, scales);
+  else
+    hipLaunchKernelGGL(moe_q::k_quantize<false>, dim3((unsigned)grid), dim3(moe_q::kThreads), 0, s, w, nblocks,
+                       packed, scales);
+  if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+  return MOE_OK;
+}

@@ -72,3 +72,21 @@ def test_strerror(moe):
     for st in range(8):
         assert moe.strerror(st)
     assert moe.strerror(99) == "unknown status"
+
+
+def test_quantize_rejects_bad_arguments(moe):
+    """moe_mxfp4_quantize validates on the host before touching the device."""
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    q = lib.moe_mxfp4_quantize
+    q.restype = ctypes.c_int
+    q.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert q(None, moe.MOE_QDTYPE_F32, 0, 64, None, None, None) == moe.MOE_OK  # nothing to do
+    assert q(None, moe.MOE_QDTYPE_F32, 4, 0, None, None, None) == moe.MOE_OK
+    assert q(None, moe.MOE_QDTYPE_F32, 4, 48, None, None, None) == moe.MOE_ESHAPE  # K % 32
+    assert q(None, 7, 4, 64, None, None, None) == moe.MOE_EINVAL  # dtype
+    assert q(None, moe.MOE_QDTYPE_BF16, -1, 64, None, None, None) == moe.MOE_EINVAL
+    assert q(None, moe.MOE_QDTYPE_F32, 4, 64, None, None, None) == moe.MOE_EINVAL  # null pointers
+    buf = ctypes.create_string_buffer(64 * 4 * 4 + 32)
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert q(base + 4, moe.MOE_QDTYPE_F32, 4, 64, base, base, None) == moe.MOE_EALIGN
