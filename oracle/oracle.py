@@ -184,3 +184,48 @@ def forward(x_bf16: np.ndarray, w_r: np.ndarray, packed: np.ndarray, scales: np.
     if np.isnan(gap):
         raise ValueError("oracle_forward rejected its arguments")
     return OracleResult(out, logits, idx, gates, offsets, sslot, pos, h, y, float(gap))
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns: first to the nearest fp32 (numpy's
+    cast, ties to even), then to the nearest bf16, ties to the even last kept
+    bit (bf16 is the top half of a binary32).  Finite inputs."""
+    f = np.ascontiguousarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+@dataclass
+class ChainResult:
+    out: np.ndarray          # r_L, fp64 [T, d]
+    layers: list             # OracleResult of every layer
+    xs: list                 # x_l (bf16 bit patterns) fed to layer l
+    min_gap: float           # smallest top-k gap over all layers
+
+
+def forward_layers(x_bf16: np.ndarray, w_r: list, packed: list, scales: list, k: int, F: int,
+                   token_mask: Optional[np.ndarray] = None, nthreads: int = 0) -> ChainResult:
+    """L MoE layers in sequence on one residual stream (the resident engine
+    running layer after layer, [P3-PK] / [P5-TRT]; reading: the pages' layer
+    is the MoE layer alone, so the stream between layers is a plain sum):
+      r_0 = x;  x_l = bf16(r_l);  r_{l+1} = r_l + MoE_l(x_l);  result r_L.
+    The rounding to bf16 decides the next layer's input, so it is taken in
+    the kernel's precision: r_l to the nearest fp32, then to the nearest bf16
+    (round_bf16).  The sums are fp64.  token_mask: every layer computes all
+    routing but only the masked tokens' expert pairs; the unmasked tokens'
+    later inputs are then not computed (so the mask is for T = 1 chains or
+    for timing only)."""
+    L = len(w_r)
+    assert len(packed) == L and len(scales) == L
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    r = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    res, xs = [], []
+    for l in range(L):
+        xs.append(x)
+        o = forward(x, w_r[l], packed[l], scales[l], k, F, token_mask=token_mask, nthreads=nthreads)
+        res.append(o)
+        r = r + o.out
+        x = round_bf16(r)
+    return ChainResult(r, res, xs, float(min(o.min_gap for o in res)))

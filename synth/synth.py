@@ -233,6 +233,16 @@ def expert_weights(cfg: Config, out_packed: Optional[np.ndarray] = None,
     return packed, scales
 
 
+def chain_layer_config(cfg: Config, layer: int) -> Config:
+    """Inputs of layer `layer` of a stack of MoE layers on one residual stream:
+    layer 0 is `cfg` itself; layer l draws its expert weights from seed
+    cfg.seed + l and its router weights from route seed cfg.route_seed + l
+    (its activations come from the layer before, not from this seed)."""
+    if layer == 0:
+        return cfg
+    return replace(cfg, name=f"{cfg.name}_layer{layer}", seed=cfg.seed + layer, route_seed=cfg.route_seed + layer)
+
+
 def algorithmic_bytes(cfg: Config, n_active: int) -> int:
     """Bytes the layer must move: each active expert's packed+scale bytes once,
     the router weights, the activations and the fp32 output."""
@@ -246,7 +256,7 @@ def layer_flops(cfg: Config) -> int:
 
 
 __all__ = [
-    "Config", "get_config", "config_names", "build", "routing_inputs", "expert_weights",
+    "Config", "get_config", "config_names", "build", "routing_inputs", "expert_weights", "chain_layer_config",
     "quantize_mxfp4", "f32_to_bf16", "bf16_to_f32", "normals", "zipf_ranks", "zipf_bias",
     "expert_packed_bytes", "expert_scale_bytes", "algorithmic_bytes", "layer_flops", "math",
 ]
