@@ -201,31 +201,47 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
 class ChainResult:
     out: np.ndarray          # r_L, fp64 [T, d]
     layers: list             # OracleResult of every layer
-    xs: list                 # x_l (bf16 bit patterns) fed to layer l
+    xs: list                 # x_l (bf16 bit patterns, normalised) fed to layer l
     min_gap: float           # smallest top-k gap over all layers
 
 
+STACK_EPS = 1e-6
+
+
+def rms_normalize(r: np.ndarray, eps: float = STACK_EPS) -> np.ndarray:
+    """Unit-gain RMS normalisation of each row: v / sqrt(mean(v^2) + eps), fp64."""
+    r = np.asarray(r, dtype=np.float64)
+    return r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+
+
 def forward_layers(x_bf16: np.ndarray, w_r: list, packed: list, scales: list, k: int, F: int,
-                   token_mask: Optional[np.ndarray] = None, nthreads: int = 0) -> ChainResult:
+                   token_mask: Optional[np.ndarray] = None, nthreads: int = 0,
+                   eps: float = STACK_EPS) -> ChainResult:
     """L MoE layers in sequence on one residual stream (the resident engine
-    running layer after layer, [P3-PK] / [P5-TRT]; reading: the pages' layer
-    is the MoE layer alone, so the stream between layers is a plain sum):
-      r_0 = x;  x_l = bf16(r_l);  r_{l+1} = r_l + MoE_l(x_l);  result r_L.
-    The rounding to bf16 decides the next layer's input, so it is taken in
-    the kernel's precision: r_l to the nearest fp32, then to the nearest bf16
-    (round_bf16).  The sums are fp64.  token_mask: every layer computes all
-    routing but only the masked tokens' expert pairs; the unmasked tokens'
-    later inputs are then not computed (so the mask is for T = 1 chains or
-    for timing only)."""
+    running the model layer after layer, [P3-PK] / [P5-TRT]).  Reading: the
+    pages describe the MoE layer alone; between two of them the stream is a
+    pre-norm residual block without its attention, whose normalisation (one
+    of the per-operator model's operators, [P3-PK]) has unit gain, as the
+    synthetic model has no trained norm weights:
+      r_0 = x;  x_l = bf16(r_l / sqrt(mean(r_l^2) + eps));
+      r_{l+1} = r_l + MoE_l(x_l);  result r_L.
+    (Without the normalisation the stream grows layer over layer: SwiGLU is
+    quadratic in its input, and eight layers of these weights overflow fp32.)
+    The rounding to bf16 decides the next layer's input, so it is taken in the
+    kernel's precision: to the nearest fp32, then to the nearest bf16
+    (round_bf16).  Sums and the normalisation are fp64.  token_mask: every
+    layer computes all routing but only the masked tokens' expert pairs, and
+    the unmasked tokens' later inputs are then not computed (so the mask is
+    for T = 1 stacks or for timing only)."""
     L = len(w_r)
     assert len(packed) == L and len(scales) == L
-    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
-    r = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    x0 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    r = (x0.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     res, xs = [], []
     for l in range(L):
+        x = round_bf16(rms_normalize(r, eps))
         xs.append(x)
         o = forward(x, w_r[l], packed[l], scales[l], k, F, token_mask=token_mask, nthreads=nthreads)
         res.append(o)
         r = r + o.out
-        x = round_bf16(r)
     return ChainResult(r, res, xs, float(min(o.min_gap for o in res)))
