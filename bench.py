@@ -59,7 +59,8 @@ def main():
                     help="untimed steps first: the GPU clocks take some tens of ms of load to ramp up")
     ap.add_argument("--workload", default="verify",
                     choices=["tiny", "decode", "verify", "batched_verify", "dense",
-                             "sweep_T4", "sweep_T16", "sweep_T22", "sweep_T32", "quantize"])
+                             "sweep_T4", "sweep_T16", "sweep_T22", "sweep_T32", "quantize", "stack_verify"])
+    ap.add_argument("--layers", type=int, default=8, help="layers of the stack_verify workload")
     ap.add_argument("--replicas", type=int, default=4, help="distinct copies of the expert weights")
     ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -84,6 +85,13 @@ def main():
             print(json.dumps({"error": "one GPU only", "n_gpus": args.gpus}))
             sys.exit(2)
         bench_quantize(args)
+        return
+
+    if args.workload == "stack_verify":
+        if args.gpus != 1:
+            print(json.dumps({"error": "one GPU only", "n_gpus": args.gpus}))
+            sys.exit(2)
+        bench_stack(args)
         return
 
     if args.gpus != 1:
@@ -229,6 +237,151 @@ def main():
             "sample": sample + f"; fp64 C oracle, {cpu_s:.2f} s wall, {nth} OpenMP threads",
             "us_per_layer": round(cpu_layer_s * 1e6, 1),
         }
+    print(json.dumps(result), flush=True)
+
+
+def bench_stack(args):
+    """A stack of L verify-block layers on one residual stream
+    (moe_mxfp4_forward_layers), timed three ways: the whole stack in one
+    resident launch, one launch per layer, and the per-layer launches captured
+    once in a HIP graph and replayed.  Layer l has its own router weights and
+    its own copy of the experts (layer 0's, relabelled by 37 l), so no layer
+    re-reads another's bytes.  Algorithmic bytes: the sum over layers of the
+    lone layer's (each layer's own active experts, found by running the
+    prefixes of the stack once)."""
+    import numpy as np
+    import torch
+
+    import mxfp4_moe_expert_router_amd as moe
+    from synth import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = args.layers
+    base = synth.get_config("verify")
+    t_gen = time.time()
+    x, _ = synth.routing_inputs(base)
+    p0, s0 = synth.expert_weights(base)
+    wr = np.stack([synth.routing_inputs(synth.chain_layer_config(base, l))[1] for l in range(L)])
+    print(f"[bench] inputs generated in {time.time() - t_gen:.1f} s (stack of {L})", file=sys.stderr, flush=True)
+    xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    wrt = torch.from_numpy(wr).to(dev)
+    pt0 = torch.from_numpy(p0).to(dev)
+    st0 = torch.from_numpy(s0).to(dev)
+    pt = torch.stack([torch.roll(pt0, -37 * l, dims=0) for l in range(L)])
+    st = torch.stack([torch.roll(st0, -37 * l, dims=0) for l in range(L)])
+    del pt0, st0
+    dims = moe.LayerDims(base.T, base.d, base.F, base.E)
+    ws = moe.alloc_workspace(dims, base.k, dev)
+    out = torch.empty((base.T, base.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    wsb = ws.numel()
+    one = moe.layers_one_launch(dims, base.k)
+
+    # every layer's active experts: the last layer of each prefix of the stack
+    n_active = []
+    for l in range(L):
+        moe.forward_layers(xt, wrt[: l + 1], pt[: l + 1], st[: l + 1], base.k, out=out, workspace=ws,
+                           flags=moe.MOE_LAYERS_PER_LAUNCH, dims=dims)
+        n_active.append(int(moe.intermediates(ws, dims, base.k)["n_active"].item()))
+    alg_bytes = sum(synth.algorithmic_bytes(base, n) for n in n_active)
+
+    def call(flags, s_handle):
+        r = moe.forward_layers_raw(dims, L, xt.data_ptr(), wrt.data_ptr(), pt.data_ptr(), st.data_ptr(), base.k,
+                                   out.data_ptr(), ws.data_ptr(), wsb, flags, s_handle)
+        if r != 0:
+            raise moe.MoeError(r, "forward_layers")
+
+    def timed(run, warm):
+        for _ in range(warm):
+            run()
+        torch.cuda.synchronize()
+        if moe.status(ws) != moe.MOE_OK:
+            raise RuntimeError("device watchdog fired")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        if moe.status(ws) != moe.MOE_OK:
+            raise RuntimeError("device watchdog fired")
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        return wall, ms
+
+    sh = stream.cuda_stream
+    modes = {}
+    warm = max(1, args.warmup // L)
+    if one:
+        modes["one_launch"] = timed(lambda: call(moe.MOE_LAYERS_ONE_LAUNCH, sh), warm)
+        ref_out = out.clone()
+    modes["launch_per_layer"] = timed(lambda: call(moe.MOE_LAYERS_PER_LAUNCH, sh), warm)
+    same = bool(torch.equal(ref_out, out)) if one else None
+    # the per-layer launches captured once, replayed
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(dev)
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        call(moe.MOE_LAYERS_PER_LAUNCH, cs.cuda_stream)  # warm the library's per-device set-up outside capture
+    stream.wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        call(moe.MOE_LAYERS_PER_LAUNCH, cs.cuda_stream)
+    torch.cuda.synchronize()
+    modes["graph_replay"] = timed(lambda: g.replay(), warm)
+    graph_same = bool(torch.equal(ref_out, out)) if one else None
+
+    main_mode = "one_launch" if one else "launch_per_layer"
+    wall, ms = modes[main_mode]
+    kern_s = float(ms.mean()) * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(alg_bytes / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "dtype_detail": "MXFP4 (E2M1 + E8M0) weights, bf16 activations, bf16x2 dot / fp32 FMA, fp32 accumulation",
+        "data": "synthetic",
+        "config": {
+            "workload": f"stack_verify: {L} layers of T={base.T} d={base.d} ffn={base.F} E={base.E} top-{base.k} "
+                        f"on one residual stream",
+            "T": base.T, "d": base.d, "ffn": base.F, "E": base.E, "topk": base.k, "layers": L,
+            "active_experts_per_layer": n_active, "path": main_mode.replace("_", " "),
+        },
+        "us_per_layer": round(wall * 1e6 / L, 2),
+        "algorithmic_bytes": alg_bytes,
+        "modes_us_per_stack": {k: {"wall": round(v[0] * 1e6, 2), "events_mean": round(float(v[1].mean()) * 1e3, 2),
+                                   "events_p10": round(float(np.percentile(v[1], 10)) * 1e3, 2),
+                                   "events_p90": round(float(np.percentile(v[1], 90)) * 1e3, 2)}
+                               for k, v in modes.items()},
+        "one_launch_equals_per_layer": same,
+        "graph_equals_one_launch": graph_same,
+        "roofline": {
+            "bound": "hbm", "achieved": round(alg_bytes / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(alg_bytes / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_stack" if one else "k_layer x L", "kernel_us_mean": round(kern_s * 1e6, 2),
+        },
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        nth = args.cpu_threads or min(16, os.cpu_count() or 1)
+        t1 = time.perf_counter()
+        oracle.forward(x, wr[0], p0, s0, base.k, base.F, nthreads=nth)
+        cpu_s = time.perf_counter() - t1
+        alg0 = synth.algorithmic_bytes(base, n_active[0])
+        result["cpu_baseline"] = {"value": round(alg0 / cpu_s / 1e9, 4), "unit": "GB/s", "cores": nth,
+                                  "kind": "oracle",
+                                  "sample": f"layer 0 of the stack (all {base.T} tokens); fp64 C oracle, "
+                                            f"{cpu_s:.2f} s wall, {nth} OpenMP threads"}
     print(json.dumps(result), flush=True)
 
 

@@ -199,9 +199,11 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
  * 32 bits are the fp32 value (the high 32 bits are a tag); logits fp32 [T][E];
  * topk_idx int32 [T][topk]; topk_w fp32 [T][topk]; offsets int32 [E+1];
  * sorted_slot, pos int32 [T*topk]; active int32 [E] (experts with at least one
- * token, ascending); n_active int32; trace: see MOE_OPT_TRACE. */
+ * token, ascending); n_active int32; trace: see MOE_OPT_TRACE; x_last bf16
+ * [T][d], after a stack call (moe_mxfp4_forward_layers) the normalised input
+ * of its last layer. */
 typedef struct {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, trace, total;
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, trace, x_last, total;
 } moe_mxfp4_ws_layout;
 int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxfp4_ws_layout* layout);
 
@@ -215,6 +217,52 @@ const char* moe_mxfp4_strerror(int status);
 /* Grid (workgroups) the persistent launch uses on the current device for these
  * sizes, or a negative moe_status. */
 int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
+
+/* ---- A stack of layers on one residual stream ([P5-TRT]: the resident
+ * engine runs the model layer after layer, each layer's MoE gate then its
+ * expert compute; [P3-PK]: the pipeline stays on the GPU between operators,
+ * whose per-operator model lists the normalisation among them).  Reading (the
+ * pages describe the MoE layer alone): a pre-norm residual block without its
+ * attention, the normalisation with unit gain (no trained weights):
+ *   r_0 = x;  x_l = bf16(r_l / sqrt(mean over d of r_l^2 + 1e-6)) (fp32
+ *   arithmetic, round to nearest even);
+ *   r_{l+1} = r_l + MoE_l(x_l) (fp32);  out = r_L.
+ *   dims, topk      as for moe_mxfp4_forward, the same for every layer
+ *   layers          L, 1 <= L <= 4096
+ *   x               bf16 [T][d], the stack's input (device, 16-byte aligned)
+ *   router_w        fp32 [L][E][d] (device, 16-byte aligned)
+ *   packed_experts  [L] x the layer's E experts, layer l at byte
+ *                   l*E*moe_mxfp4_expert_packed_bytes(d, F) (device, 16-byte aligned)
+ *   scales          [L] x the layer's E experts, layer l at byte
+ *                   l*E*moe_mxfp4_expert_scale_bytes(d, F) (device)
+ *   out             fp32 [T][d] = r_L (device, 16-byte aligned, fully
+ *                   overwritten; it holds r_l while the stack runs, so it
+ *                   must not overlap any input)
+ *   workspace       as for moe_mxfp4_forward (same size).  After the call its
+ *                   inspection copies describe the last layer, and x_last
+ *                   (moe_mxfp4_ws_layout) holds that layer's input.
+ *   flags           0: the whole stack in ONE resident launch when the sizes
+ *                   take the small-batch path with x of every token in LDS
+ *                   (moe_mxfp4_layers_one_launch), else one launch per layer;
+ *                   MOE_LAYERS_PER_LAUNCH: always one launch per operator
+ *                   (per layer: the normalisation, then the layer);
+ *                   MOE_LAYERS_ONE_LAUNCH: one launch, or MOE_ESHAPE.
+ * In the one launch, the workgroups meet between layers: each publishes its
+ * part of the stream and raises an arrival word; once every arrival word has
+ * moved on, each workgroup normalises the stream into its LDS and the next
+ * layer's router starts (its first weight loads are issued before the wait).  Errors as moe_mxfp4_forward, and
+ * MOE_EINVAL for L out of range or unknown / conflicting flags.  A device
+ * wait that times out stops the stack (MOE_ETIMEOUT from moe_mxfp4_status;
+ * out is then undefined). */
+#define MOE_LAYERS_PER_LAUNCH 0x1
+#define MOE_LAYERS_ONE_LAUNCH 0x2
+int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const void* x, const float* router_w,
+                             const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                             void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
+
+/* 1 if moe_mxfp4_forward_layers runs these sizes in one launch by default, 0 if
+ * it takes one launch per layer, or a negative moe_status. */
+int moe_mxfp4_layers_one_launch(const moe_mxfp4_dims* dims, int32_t topk);
 
 /* ---- MXFP4 quantize / pack on the GPU ([P3-FP4] 4-bit values with a shared
  * per-block scale; [MX] conversion): the direction opposite to the layer's

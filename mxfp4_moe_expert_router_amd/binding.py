@@ -22,6 +22,8 @@ MOE_OPT_WITHHOLD_ARRIVAL = 0x1
 MOE_OPT_TRACE = 0x2
 MOE_OPT_COOPERATIVE = 0x4
 MOE_QDTYPE_F32, MOE_QDTYPE_BF16 = 0, 1
+MOE_LAYERS_PER_LAUNCH = 0x1
+MOE_LAYERS_ONE_LAUNCH = 0x2
 
 
 class MoeError(RuntimeError):
@@ -41,7 +43,7 @@ class Options(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_idx", "topk_w", "offsets", "sorted_slot", "pos", "active", "n_active", "h", "y", "trace",
-                 "total")]
+                 "x_last", "total")]
 
 
 def _load():
@@ -77,6 +79,10 @@ def _load():
     lib.moe_mxfp4_persistent_grid.restype = ctypes.c_int
     lib.moe_mxfp4_persistent_grid.argtypes = [P(Dims), i32]
     lib.moe_mxfp4_quantize.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_layers.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_layers.argtypes = [P(Dims), i32, vp, vp, vp, vp, i32, vp, vp, sz, i32, vp]
+    lib.moe_mxfp4_layers_one_launch.restype = ctypes.c_int
+    lib.moe_mxfp4_layers_one_launch.argtypes = [P(Dims), i32]
     lib.moe_mxfp4_quantize.argtypes = [vp, i32, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
     return lib
 
@@ -199,6 +205,46 @@ def forward_raw(dims: LayerDims, x_ptr: int, wr_ptr: int, packed_ptr: int, scale
               stream_handle)
 
 
+def forward_layers(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, topk: int,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                   stream=None, dims: Optional[LayerDims] = None) -> torch.Tensor:
+    """A stack of L MoE layers on one residual stream, each on the unit-gain RMS
+    normalised stream (moe_mxfp4_forward_layers):
+    x bf16 [T, d]; router_w fp32 [L, E, d]; packed uint8 [L, E, 3*d*ffn/2];
+    scales uint8 [L, E, 3*d*ffn/32]; returns out fp32 [T, d] = r_L."""
+    if router_w.dim() != 3 or packed.dim() != 3 or scales.dim() != 3:
+        raise ValueError("router_w, packed and scales must be [L, E, ...]")
+    L, E, d = router_w.shape
+    if packed.shape[:2] != (L, E) or scales.shape[:2] != (L, E):
+        raise ValueError("router_w, packed and scales disagree on L or E")
+    dims = dims or LayerDims(int(x.shape[0]), int(d), int(packed.shape[2] * 2 // (3 * d)), int(E))
+    if out is None:
+        out = torch.empty((dims.T, dims.d), dtype=torch.float32, device=x.device)
+    _validate(x, router_w, packed, scales, out)
+    if workspace is None:
+        workspace = alloc_workspace(dims, topk, x.device)
+    st = lib.moe_mxfp4_forward_layers(ctypes.byref(dims.c()), int(L), _ptr(x), _ptr(router_w), _ptr(packed),
+                                      _ptr(scales), int(topk), _ptr(out), _ptr(workspace), workspace.numel(),
+                                      int(flags), _stream(stream))
+    _check(st, "moe_mxfp4_forward_layers")
+    return out
+
+
+def forward_layers_raw(dims: LayerDims, layers: int, x_ptr: int, wr_ptr: int, packed_ptr: int, scales_ptr: int,
+                       topk: int, out_ptr: int, ws_ptr: int, ws_bytes: int, flags: int, stream_handle: int) -> int:
+    """Unchecked pointer-level stack call (bench loops); returns the status."""
+    return lib.moe_mxfp4_forward_layers(ctypes.byref(dims.c()), layers, x_ptr, wr_ptr, packed_ptr, scales_ptr, topk,
+                                        out_ptr, ws_ptr, ws_bytes, flags, stream_handle)
+
+
+def layers_one_launch(dims: LayerDims, topk: int) -> bool:
+    """True if forward_layers runs these sizes as one launch by default."""
+    r = lib.moe_mxfp4_layers_one_launch(ctypes.byref(dims.c()), topk)
+    if r < 0:
+        raise MoeError(-r, "layers_one_launch")
+    return bool(r)
+
+
 def route(x: torch.Tensor, router_w: torch.Tensor, topk: int, ffn: int, workspace: Optional[torch.Tensor] = None,
           stream=None):
     """Routing only: (topk_idx int32 [T,k], topk_w fp32 [T,k], offsets int32 [E+1], sorted_slot int32 [T*k])."""
@@ -253,6 +299,7 @@ def intermediates(workspace: torch.Tensor, dims: LayerDims, topk: int) -> dict:
         "h": tagged(lay.h, TK * F).view(TK, F),
         "y": tagged(lay.y, TK * d).view(TK, d),
         "trace": view(lay.trace, 2048 * 16, torch.int64).view(2048, 16),
+        "x_last": view(lay.x_last, T * d, torch.int16).view(T, d),
     }
 
 

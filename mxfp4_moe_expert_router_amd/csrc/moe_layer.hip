@@ -75,6 +75,7 @@ constexpr int kGUChunks = 4;           // 16-byte chunks per lane of a d-row (d 
 constexpr int kGUTok = 4;              // tokens per pass over a decoded gate/up row pair
 constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
 constexpr int kMaxGrid = 2048;
+constexpr int kMaxLayers = 4096;        // layers of one stack call
 constexpr int kMaxMaskWords = 4096;    // E * ceil(T/64)
 constexpr int kTraceSlots = 16;        // wall-clock stamps per workgroup (trace option)
 constexpr int kTopkRep = 8;            // copies of the top-k results (each read by 1/8 of the grid)
@@ -121,6 +122,17 @@ struct Params {
   int mfma;           // 1: x does not fit in LDS, expert steps on MFMA
   int xmode;          // small-batch path: 0 x of every token in LDS, 1 x of the workgroup's pairs (see stage_pairs)
   int xrows;          // small-batch path: rows of x the LDS holds
+  // A stack of layers on one residual stream r (r_0 = x0, x_l =
+  // bf16(rmsnorm(r_l)), r_{l+1} = r_l + layer_l(x_l), out = r_L): the combine
+  // adds the layer's output to r, which out holds.
+  int stack_layers;   // L of the stack; 0: a lone layer (out = layer(x))
+  int layer0;         // stack index of the launch's first layer
+  int nlayers;        // layers this launch runs (k_stack), 1 otherwise
+  const uint16_t* x0; // the stack's input, bf16 [T][d] (r_0)
+  uint16_t* xb;       // bf16 [T][d]: a layer's normalised input (the last one's after a call)
+  size_t wr_stride;   // floats between layers' router weights
+  size_t pk_stride;   // bytes between layers' packed experts
+  size_t sc_stride;   // bytes between layers' scales
 };
 
 // ------------------------------------------------------------ LDS layout ----
@@ -208,7 +220,7 @@ __device__ __forceinline__ bool aborted(const Params& P, uint32_t tag) {
 }
 
 // Wait sites, recorded with the index waited on when a watchdog fires.
-enum { kSiteLogits = 1, kSiteTopk = 2, kSiteH = 3, kSiteY = 4, kSiteStarted = 5 };
+enum { kSiteLogits = 1, kSiteTopk = 2, kSiteH = 3, kSiteY = 4, kSiteStarted = 5, kSiteLayer = 6 };
 
 __device__ __forceinline__ void raise_timeout(const Params& P, uint32_t tag, uint32_t site, uint32_t what) {
   st_relaxed(&P.hdr[kWhere], site);
@@ -241,10 +253,13 @@ __device__ __forceinline__ bool keep_waiting(const Params& P, uint32_t tag, uint
 }
 
 // Tag of this call: epoch + 1, never 0 (a zero-filled workspace has tag 0).
-__device__ __forceinline__ uint32_t start_call(const Params& P, int wg, bool mark_started) {
+// A launch that runs `nl` layers uses tags epoch + 1 .. epoch + nl, one per
+// layer; they restart from 1 rather than reach 0xFFFFFFFF.
+__device__ __forceinline__ uint32_t start_call(const Params& P, int wg, bool mark_started, int nl = 1) {
   __shared__ uint32_t s_tag;
   if (threadIdx.x == 0) {
-    const uint32_t e = ld_relaxed(&P.hdr[kEpoch]);
+    uint32_t e = ld_relaxed(&P.hdr[kEpoch]);
+    if (e > 0xFFFFFFFEu - (uint32_t)nl) e = 0u;
     s_tag = e + 1u;
     if (mark_started) st_relaxed(&P.hdr[kStarted + wg], e + 1u);
   }
@@ -1952,7 +1967,16 @@ __device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32
 // ---------------------------------------------------------- combine ---------
 // out[t][c] = sum over j < k of the tagged gated rows y[t*k + j][c], in slot
 // order.  Unit = (token, 64 columns), one wave.
-__device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW) {
+// In a stack (P.stack_layers > 0) the sum goes onto the residual stream:
+// r = (layer 0 ? x0 : out) + sum, written to out with agent-scope
+// (write-through) stores, which the next layer's workgroups read after the
+// arrival wait without a write-back of the L2.  Each element of out is read
+// and written by the same wave in every layer.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite f
+}
+__device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW, int layer) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int kCols = 2 * kWave;  // two columns (one 16-byte load of tagged words) per lane
   const int nd = (P.d + kCols - 1) / kCols;
@@ -1973,7 +1997,25 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
         a1 += u2f(q.z);
       }
       if (__all(ok)) {
-        if (c < P.d) *reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c) = make_float2(a0, a1);
+        if (c < P.d) {
+          float2* o = reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c);
+          if (P.stack_layers > 0) {  // uniform
+            if (layer == 0) {
+              const uint32_t xv = *reinterpret_cast<const uint32_t*>(P.x0 + (size_t)t * P.d + c);
+              a0 = bf16lo(xv) + a0;
+              a1 = bf16hi(xv) + a1;
+            } else {
+              const float2 r = *o;
+              a0 = r.x + a0;
+              a1 = r.y + a1;
+            }
+            const uint64_t bits = (uint64_t)__builtin_bit_cast(uint32_t, a0) |
+                                  ((uint64_t)__builtin_bit_cast(uint32_t, a1) << 32);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(o), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            *o = make_float2(a0, a1);
+          }
+        }
         break;
       }
       if (!keep_waiting(P, tag, t0, kSiteY, u, round, 3)) return false;
@@ -2041,11 +2083,198 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
       down_mfma(P, S, tag, wg, G);
     }
     stamp(P, wg, 5);
-    if (dn) combine_step(P, tag, gw, NW);
+    if (dn) combine_step(P, tag, gw, NW, P.layer0);
     stamp(P, wg, 6);
   }
   __syncthreads();
   if (wg == 0) end_call(P, tag, G);
+}
+
+// ------------------------------------------------- normalised layer input --
+// Input of a layer of a stack: x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)),
+// unit gain, eps = 1e-6, round to nearest even ([P3-PK] lists the
+// normalisation among the operators between layers).  r_l is fp32 [T][d] at
+// rf, or for layer 0 the stack's bf16 input rb.  Rows t0..t1-1, one at a time,
+// by the whole workgroup: thread i takes the row's 8-element pieces i, i +
+// kWG, ... and sums their squares in order, each wave adds its lanes in a
+// fixed butterfly, and the 8 wave sums are added in wave order, so every
+// workgroup that normalises a row (and k_norm) gets the same bits.  A scaled
+// piece goes to the piece-transposed LDS rows of stage_x (xs, row t - t0)
+// and/or to row t of xg (bf16, row-major).  All threads.
+constexpr float kStackEps = 1e-6f;
+__device__ __forceinline__ void norm_piece(const Params& P, const float* rf, const uint16_t* rb, int t, int i,
+                                           float (&v)[8]) {
+  if (rb != nullptr) {
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rb + (size_t)t * P.d + 8 * i);
+    v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+    v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+  } else {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(rf + (size_t)t * P.d + 8 * i);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(rf + (size_t)t * P.d + 8 * i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+__device__ void norm_rows(const Params& P, const float* rf, const uint16_t* rb, int t0, int t1, u32x4_t* xs,
+                          uint16_t* xg) {
+  __shared__ float s_ss[kWaves];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int NCH = P.d / 32, npc = P.d / 8;
+  for (int t = t0; t < t1; ++t) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < npc; i += kWG) {
+      float v[8];
+      norm_piece(P, rf, rb, t, i, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (lane == 0) s_ss[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += s_ss[w];
+    const float inv = 1.f / sqrtf(tot / (float)P.d + kStackEps);
+    for (int i = threadIdx.x; i < npc; i += kWG) {
+      float v[8];
+      norm_piece(P, rf, rb, t, i, v);
+      u32x4_t q;
+      q.x = bf16_rne(v[0] * inv) | (bf16_rne(v[1] * inv) << 16);
+      q.y = bf16_rne(v[2] * inv) | (bf16_rne(v[3] * inv) << 16);
+      q.z = bf16_rne(v[4] * inv) | (bf16_rne(v[5] * inv) << 16);
+      q.w = bf16_rne(v[6] * inv) | (bf16_rne(v[7] * inv) << 16);
+      if (xs != nullptr) xs[(size_t)(t - t0) * 4 * NCH + (i % 4) * NCH + i / 4] = q;
+      if (xg != nullptr) *reinterpret_cast<u32x4_t*>(xg + (size_t)t * P.d + 8 * i) = q;
+    }
+    __syncthreads();  // s_ss is reused by the next row
+  }
+}
+
+// One launch per layer: the layer's input, one row per workgroup.
+__global__ void __launch_bounds__(kWG) k_norm(Params P) {
+  const bool first = P.layer0 == 0;
+  norm_rows(P, first ? nullptr : P.out, first ? P.x0 : nullptr, blockIdx.x, blockIdx.x + 1, nullptr, P.xb);
+}
+
+// ------------------------------------------------- a stack in one launch ---
+// Layer after layer of a stack inside one resident launch ([P3-PK]: the
+// pipeline stays on the GPU, no return to the host between operators;
+// [P5-TRT]: MoE gate then expert compute, per layer).  Layer l runs under tag
+// t0 + l.  Between layers every workgroup publishes its part of the stream r
+// (the combine's write-through stores; each wave waits for them to complete),
+// then its arrival word (hdr[kStarted + wg]) takes the next layer's tag.  The
+// next layer's router needs the input of every token, so each workgroup waits
+// until every arrival word has reached that tag, then acquires (which drops
+// its CU's and XCD's cached lines) and normalises r into LDS itself (every
+// workgroup gets the same bits, see norm_rows).  The router's first weight
+// loads are already in flight during that wait.
+
+// Tags of this launch lie in [t0, t0 + nl): a raised abort word in that range
+// stops the stack.
+__device__ __forceinline__ bool stack_aborted(const Params& P, uint32_t t0) {
+  return ld_relaxed(&P.hdr[kAbort]) - t0 < (uint32_t)P.nlayers;
+}
+
+// Wave 0: every workgroup's arrival word has reached `tag` (a signed
+// difference, so that the words of earlier launches, including those from
+// before the tags restarted at 1, count as behind it).  False if the wait was
+// abandoned.
+__device__ __forceinline__ bool wait_arrivals(const Params& P, uint32_t t0, uint32_t tag, int G) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t ts = wall_clock64();
+  int round = 0;
+  for (;;) {
+    bool ok = true;
+    for (int w = lane; w < G; w += kWave) ok &= (int32_t)(ld_relaxed(&P.hdr[kStarted + w]) - tag) >= 0;
+    if (__all(ok)) return true;
+    if ((round & 7) == 7 && stack_aborted(P, t0)) return false;
+    if (wall_clock64() - ts > P.spin_ticks) {
+      if (lane == 0) raise_timeout(P, tag, kSiteLayer, 0);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    ++round;
+    __asm__ __volatile__("" ::: "memory");
+  }
+}
+
+template <int V, int MM>
+__global__ void __launch_bounds__(kWG) k_stack(Params P0) {
+  static_assert(V == kVAll || V == kVAllH, "stacks keep x of every token in LDS");
+  constexpr bool HS = V == kVAllH;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_ok, s_go;
+  const Smem S = carve(smem, P0, true);
+  const int wg = blockIdx.x, G = gridDim.x;
+  const int gw = wg * kWaves + uni(threadIdx.x / kWave), NW = G * kWaves;
+  const uint32_t t0 = start_call(P0, wg, true, P0.nlayers);
+  const uint32_t tlast = t0 + (uint32_t)P0.nlayers - 1u;
+  Params P = P0;
+  int l = 0;
+  uint32_t tag = t0;
+  int sl = P0.layer0;
+  // The layer loop is entered at its top, and (never: the host passes
+  // nlayers >= 1) at its second half: a cycle with two entries is not a
+  // natural loop, so the optimizer hoists none of the body's lane-invariant
+  // values out of it, which would hold them in registers across the whole
+  // layer (measured: ~190 VGPR spills with the plain loop, none without).
+  if (P0.nlayers < 1) goto second_half;
+  for (;;) {
+    tag = t0 + (uint32_t)l;
+    sl = P0.layer0 + l;
+    P.wr = P0.wr + (size_t)l * P0.wr_stride;
+    P.packed = P0.packed + (size_t)l * P0.pk_stride;
+    P.scales = P0.scales + (size_t)l * P0.sc_stride;
+    if (threadIdx.x == 0) s_ok = s_go = 1;
+    __syncthreads();
+    router_step<true>(P, S, tag, wg, G, [&] {
+      if (l > 0) {
+        if (threadIdx.x < kWave) {
+          const bool ok = wait_arrivals(P, t0, tag, G);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          if (!ok && threadIdx.x == 0) s_go = 0;
+        }
+        __syncthreads();
+      }
+      // workgroup 0 also leaves the last layer's input in xb, for inspection
+      if (s_go)
+        norm_rows(P, sl == 0 ? nullptr : P.out, sl == 0 ? P.x0 : nullptr, 0, P.T, S.xs,
+                  (wg == 0 && l == P0.nlayers - 1) ? P0.xb : nullptr);
+      __syncthreads();
+    });
+    if (!s_go) break;  // uniform
+  second_half:
+    {
+      bool ok = topk_publish(P, tag, gw, NW);
+      __syncthreads();
+      ok = load_topk(P, S, tag, wg % kTopkRep) && ok;
+      __syncthreads();
+      if (!ok) s_ok = 0;
+      __syncthreads();
+      if (!s_ok) break;  // uniform
+      build_perm(P, S, wg == 0);
+      set_ranges(P, S, wg, G);
+      if (wg < 8 && threadIdx.x >= kWG - kWave) invalidate_l2();
+      gate_up_waves<false>(P, S, tag, wg, G);
+      bool dn = down_dispatch<MM, HS>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
+      if (dn) dn = combine_step(P, tag, gw, NW, sl);
+      if (!dn) s_ok = 0;
+      // this wave's write-through stores of r have completed before the arrival
+      __builtin_amdgcn_s_waitcnt(0);
+      if (threadIdx.x == 0 && stack_aborted(P0, t0)) s_ok = 0;
+      __syncthreads();
+      if (!s_ok) break;  // uniform
+    }
+    if (++l >= P0.nlayers) break;
+    if (threadIdx.x == 0) st_relaxed(&P0.hdr[kStarted + wg], tag + 1u);
+  }
+  // a workgroup that stopped early still closes its arrival word, so that
+  // the end of the launch does not wait for it
+  __syncthreads();
+  if (threadIdx.x == 0) st_relaxed(&P0.hdr[kStarted + wg], tlast);
+  __syncthreads();
+  if (wg == 0) end_call(P0, tlast, G);
 }
 
 // One launch per step (the per-operator model), same arithmetic.
@@ -2123,7 +2352,7 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
-  combine_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves);
+  combine_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves, P.layer0);
 }
 __global__ void k_st_bump(Params P) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
@@ -2153,7 +2382,7 @@ static int check_dims(const moe_mxfp4_dims* dm, int32_t topk) {
 }
 
 struct Layout {
-  size_t hdr, lgp, tk, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, trace,
+  size_t hdr, lgp, tk, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, trace, xb,
       total;
 };
 
@@ -2175,6 +2404,7 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
   L.active = o; o = align_up(o + E * 4);
   L.n_active = o; o = align_up(o + 4);
   L.trace = o; o = align_up(o + (size_t)kMaxGrid * kTraceSlots * 8);
+  L.xb = o; o = align_up(o + T * (size_t)dm->d * 2);
   L.total = o;
   return L;
 }
@@ -2206,6 +2436,13 @@ static const void* layer_kernel(int v, int mm) {
   }
 }
 
+// The one-launch stack: small-batch path with x of every token in LDS.
+static const void* stack_kernel(int v, int mm) {
+  if (v == kVAllH) return (const void*)k_stack<kVAllH, 1>;
+  if (v == kVAll) return mm == 1 ? (const void*)k_stack<kVAll, 1> : (const void*)k_stack<kVAll, 2>;
+  return nullptr;
+}
+
 static int device_info(DeviceInfo* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
@@ -2217,7 +2454,8 @@ static int device_info(DeviceInfo* out) {
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_EDEVICE;
     const void* ks[] = {layer_kernel(kVAll, 1), layer_kernel(kVAll, 2), layer_kernel(kVAllH, 1),
                         layer_kernel(kVPairs, 1), layer_kernel(kVPairs, 2), layer_kernel(kVMfma, 1),
-                        layer_kernel(kVMfma, 2),
+                        layer_kernel(kVMfma, 2), stack_kernel(kVAll, 1), stack_kernel(kVAll, 2),
+                        stack_kernel(kVAllH, 1),
                         (const void*)k_st_perm, (const void*)k_st_gate_up<true>, (const void*)k_st_gate_up<false>,
                         (const void*)k_st_down<0>, (const void*)k_st_down<1>, (const void*)k_st_down<2>};
     for (const void* f : ks) {
@@ -2277,6 +2515,12 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.mfma = 0;
   P.xmode = 0;
   P.xrows = 0;
+  P.stack_layers = 0;
+  P.layer0 = 0;
+  P.nlayers = 1;
+  P.xb = reinterpret_cast<uint16_t*>(b + L.xb);
+  P.x0 = static_cast<const uint16_t*>(x);
+  P.wr_stride = P.pk_stride = P.sc_stride = 0;
   return P;
 }
 
@@ -2420,6 +2664,7 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxf
   out->h = L.hq;
   out->y = L.yq;
   out->trace = L.trace;
+  out->x_last = L.xb;
   out->total = L.total;
   return MOE_OK;
 }
@@ -2531,6 +2776,70 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
     return MOE_EDEVICE;
   if (sorted_slot && hipMemcpyAsync(sorted_slot, P.sorted_slot, TK * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return MOE_EDEVICE;
+  return MOE_OK;
+}
+
+int moe_mxfp4_layers_one_launch(const moe_mxfp4_dims* dims, int32_t topk) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return -st;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return -st;
+  return stack_kernel(L.v, L.mm) != nullptr ? 1 : 0;
+}
+
+int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const void* x, const float* router_w,
+                             const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                             void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (layers < 1 || layers > kMaxLayers) return MOE_EINVAL;
+  if (flags & ~(MOE_LAYERS_PER_LAUNCH | MOE_LAYERS_ONE_LAUNCH)) return MOE_EINVAL;
+  if ((flags & MOE_LAYERS_PER_LAUNCH) && (flags & MOE_LAYERS_ONE_LAUNCH)) return MOE_EINVAL;
+  if (dims->T == 0) return MOE_OK;
+  st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
+  if (st != MOE_OK) return st;
+  if (workspace_bytes < make_layout(dims, topk).total) return MOE_EWORKSPACE;
+  Launch L;
+  st = plan_launch(dims, topk, &L);
+  if (st != MOE_OK) return st;
+  const void* sk = stack_kernel(L.v, L.mm);
+  if ((flags & MOE_LAYERS_ONE_LAUNCH) && !sk) return MOE_ESHAPE;
+  DeviceInfo di;
+  st = device_info(&di);
+  if (st != MOE_OK) return st;
+  Params P = make_params(dims, topk, x, router_w, packed_experts, scales, out, workspace, di, 0u);
+  apply_launch(P, L);
+  P.stack_layers = layers;
+  P.wr_stride = (size_t)dims->E * dims->d;
+  P.pk_stride = (size_t)dims->E * moe_mxfp4_expert_packed_bytes(dims->d, dims->ffn);
+  P.sc_stride = (size_t)dims->E * moe_mxfp4_expert_scale_bytes(dims->d, dims->ffn);
+  hipStream_t s = (hipStream_t)stream;
+  if (sk && !(flags & MOE_LAYERS_PER_LAUNCH)) {
+    P.nlayers = layers;
+    void* args[] = {&P};
+    const int grid = grid_for(di, sk, L.lds, 0);
+    if (hipLaunchKernel(sk, dim3(grid), dim3(kWG), args, (unsigned)L.lds, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ELAUNCH;
+    }
+    return MOE_OK;
+  }
+  // one launch per operator: per layer, the normalisation of its input into
+  // xb, then a lone-layer launch on xb that adds onto the stream
+  const int grid = grid_for(di, layer_kernel(L.v, L.mm), L.lds, 0);
+  for (int l = 0; l < layers; ++l) {
+    Params Q = P;
+    Q.layer0 = l;
+    Q.wr = P.wr + (size_t)l * P.wr_stride;
+    Q.packed = P.packed + (size_t)l * P.pk_stride;
+    Q.scales = P.scales + (size_t)l * P.sc_stride;
+    Q.x = P.xb;
+    hipLaunchKernelGGL(k_norm, dim3(dims->T), dim3(kWG), 0, s, Q);
+    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    st = launch_layer(Q, L, grid, s, false);
+    if (st != MOE_OK) return st;
+  }
   return MOE_OK;
 }
 

@@ -25,3 +25,12 @@ def synth_mod():
     from synth import synth
     synth.build()
     return synth
+
+
+@pytest.fixture(scope="session")
+def verify_experts(synth_mod):
+    """The 256 MXFP4 experts of the full-size workloads (d=7168, ffn=2048), host
+    arrays, generated once per session."""
+    cfg = synth_mod.get_config("verify")
+    print("\n[full] generating 256 MXFP4 experts (d=7168, ffn=2048)", flush=True)
+    return synth_mod.expert_weights(cfg)

@@ -90,3 +90,34 @@ def test_quantize_rejects_bad_arguments(moe):
     buf = ctypes.create_string_buffer(64 * 4 * 4 + 32)
     base = (ctypes.addressof(buf) + 15) // 16 * 16
     assert q(base + 4, moe.MOE_QDTYPE_F32, 4, 64, base, base, None) == moe.MOE_EALIGN
+
+
+def _call_layers(moe, dims, layers=2, topk=2, flags=0, x=256, wr=256, p=256, s=256, out=256, ws=256, wsb=1 << 30):
+    D = moe.binding.Dims(*dims)
+    return moe.binding.lib.moe_mxfp4_forward_layers(ctypes.byref(D), layers, x, wr, p, s, topk, out, ws, wsb, flags,
+                                                    None)
+
+
+def test_layers_validation_codes(moe):
+    ok_dims = (4, 64, 32, 8)
+    assert _call_layers(moe, ok_dims, layers=0) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, layers=4097) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, flags=4) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, flags=moe.MOE_LAYERS_PER_LAUNCH | moe.MOE_LAYERS_ONE_LAUNCH) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, x=0) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, topk=9) == moe.MOE_EINVAL
+    assert _call_layers(moe, (4, 48, 32, 8)) == moe.MOE_ESHAPE
+    assert _call_layers(moe, ok_dims, out=264) == moe.MOE_EALIGN
+    assert _call_layers(moe, ok_dims, wsb=1024) == moe.MOE_EWORKSPACE
+    assert _call_layers(moe, (0, 64, 32, 8), x=0, out=0) == moe.MOE_OK
+    # the dense batch takes the MFMA path: one launch per layer only
+    assert _call_layers(moe, (512, 7168, 2048, 256), topk=8, flags=moe.MOE_LAYERS_ONE_LAUNCH) == moe.MOE_ESHAPE
+
+
+def test_layers_one_launch_choice(moe):
+    assert moe.layers_one_launch(moe.LayerDims(8, 7168, 2048, 256), 8)      # verify block: x of all tokens in LDS
+    assert moe.layers_one_launch(moe.LayerDims(1, 7168, 2048, 256), 8)      # decode
+    assert not moe.layers_one_launch(moe.LayerDims(32, 7168, 2048, 256), 8)  # x rows of the workgroup's pairs
+    assert not moe.layers_one_launch(moe.LayerDims(512, 7168, 2048, 256), 8)  # MFMA path
+    with pytest.raises(moe.MoeError):
+        moe.layers_one_launch(moe.LayerDims(4, 48, 32, 8), 2)

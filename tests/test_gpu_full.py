@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module")
-def full_env():
+def full_env(verify_experts):
     import torch
 
     import mxfp4_moe_expert_router_amd as moe
@@ -26,9 +26,7 @@ def full_env():
 
     oracle.build()
     synth.build()
-    cfg = synth.get_config("verify")
-    print("\n[full] generating 256 MXFP4 experts (d=7168, ffn=2048)", flush=True)
-    p, s = synth.expert_weights(cfg)
+    p, s = verify_experts
     pt = torch.from_numpy(p).cuda()
     st = torch.from_numpy(s).cuda()
     torch.cuda.synchronize()
