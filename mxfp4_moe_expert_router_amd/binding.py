@@ -238,7 +238,7 @@ def forward_layers_raw(dims: LayerDims, layers: int, x_ptr: int, wr_ptr: int, pa
 
 
 def layers_one_launch(dims: LayerDims, topk: int) -> bool:
-    """True if forward_layers runs these sizes as one launch by default."""
+    """True if forward_layers can run these sizes as one resident launch (MOE_LAYERS_ONE_LAUNCH)."""
     r = lib.moe_mxfp4_layers_one_launch(ctypes.byref(dims.c()), topk)
     if r < 0:
         raise MoeError(-r, "layers_one_launch")

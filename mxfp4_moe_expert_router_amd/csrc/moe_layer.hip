@@ -2027,10 +2027,11 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
 // ---------------------------------------------------------- kernels ---------
 
 // Expert-step variants of the whole-layer kernel (the host picks one, see
-// plan_launch): kVAll, x of every token in LDS; kVAllH, the same with the down
-// step's h staged per workgroup (stage_h, for few units per workgroup);
-// kVPairs, x of each workgroup's own pairs in LDS and h staged; kVMfma, the
-// MFMA expert steps.
+// plan_launch): kVAll, x of every token in LDS (two W_down chunks per lane);
+// kVAllH, the same with the down step's h staged per workgroup where it pays
+// (stage_h: experts of more than two tokens, or few units per workgroup; one
+// W_down chunk per lane); kVPairs, x of each workgroup's own pairs in LDS and
+// h staged; kVMfma, the MFMA expert steps.
 constexpr int kVAll = 0, kVAllH = 1, kVPairs = 2, kVMfma = 3;
 
 // The whole layer in one launch.  V: variant; MM: W_down chunks per lane.
@@ -2094,60 +2095,84 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
 // Input of a layer of a stack: x_l = bf16(r_l / sqrt(mean(r_l^2) + eps)),
 // unit gain, eps = 1e-6, round to nearest even ([P3-PK] lists the
 // normalisation among the operators between layers).  r_l is fp32 [T][d] at
-// rf, or for layer 0 the stack's bf16 input rb.  Rows t0..t1-1, one at a time,
-// by the whole workgroup: thread i takes the row's 8-element pieces i, i +
-// kWG, ... and sums their squares in order, each wave adds its lanes in a
-// fixed butterfly, and the 8 wave sums are added in wave order, so every
+// rf, or for layer 0 the stack's bf16 input rb.  Rows t0..t1-1 in groups of
+// kNormRows, by the whole workgroup: thread i holds the row's 8-element pieces
+// i and i + kWG (d <= 8192) of every row of the group in registers (one round
+// of loads per group), sums their squares in order, each wave adds its lanes
+// in a fixed butterfly and the 8 wave sums are added in wave order, so every
 // workgroup that normalises a row (and k_norm) gets the same bits.  A scaled
 // piece goes to the piece-transposed LDS rows of stage_x (xs, row t - t0)
-// and/or to row t of xg (bf16, row-major).  All threads.
+// and/or to row t of xg (bf16, row-major).  All threads.  (Groups of 2 rows:
+// 4 rows in flight pushed the resident stack kernel's registers into scratch.)
 constexpr float kStackEps = 1e-6f;
-__device__ __forceinline__ void norm_piece(const Params& P, const float* rf, const uint16_t* rb, int t, int i,
-                                           float (&v)[8]) {
-  if (rb != nullptr) {
-    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rb + (size_t)t * P.d + 8 * i);
-    v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
-    v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
-  } else {
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(rf + (size_t)t * P.d + 8 * i);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(rf + (size_t)t * P.d + 8 * i + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
+constexpr int kNormRows = 2;
 __device__ void norm_rows(const Params& P, const float* rf, const uint16_t* rb, int t0, int t1, u32x4_t* xs,
                           uint16_t* xg) {
-  __shared__ float s_ss[kWaves];
+  __shared__ float s_ss[kNormRows][kWaves];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int NCH = P.d / 32, npc = P.d / 8;
-  for (int t = t0; t < t1; ++t) {
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < npc; i += kWG) {
-      float v[8];
-      norm_piece(P, rf, rb, t, i, v);
+  const int i0 = threadIdx.x, i1 = threadIdx.x + kWG;
+  const bool h0 = i0 < npc, h1 = i1 < npc;  // pieces this thread holds
+  for (int g0 = t0; g0 < t1; g0 += kNormRows) {
+    const int ng = min(kNormRows, t1 - g0);
+    float v[kNormRows][2][8];
+    // loads: every row of the group, both pieces (absent ones read piece 0
+    // and are not used)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+    for (int r = 0; r < kNormRows; ++r) {
+      const int t = g0 + min(r, ng - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = (h == 0 ? h0 : h1) ? (h == 0 ? i0 : i1) : 0;
+        if (rb != nullptr) {  // uniform
+          const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rb + (size_t)t * P.d + 8 * i);
+          v[r][h][0] = bf16lo(q.x); v[r][h][1] = bf16hi(q.x); v[r][h][2] = bf16lo(q.y); v[r][h][3] = bf16hi(q.y);
+          v[r][h][4] = bf16lo(q.z); v[r][h][5] = bf16hi(q.z); v[r][h][6] = bf16lo(q.w); v[r][h][7] = bf16hi(q.w);
+        } else {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(rf + (size_t)t * P.d + 8 * i);
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(rf + (size_t)t * P.d + 8 * i + 4);
+          v[r][h][0] = u2f(a.x); v[r][h][1] = u2f(a.y); v[r][h][2] = u2f(a.z); v[r][h][3] = u2f(a.w);
+          v[r][h][4] = u2f(b.x); v[r][h][5] = u2f(b.y); v[r][h][6] = u2f(b.z); v[r][h][7] = u2f(b.w);
+        }
+      }
     }
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    if (lane == 0) s_ss[wave] = ss;
+    for (int r = 0; r < kNormRows; ++r) {
+      float ss = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (h == 0 ? h0 : h1)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fmaf(v[r][h][j], v[r][h][j], ss);
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      if (lane == 0) s_ss[r][wave] = ss;
+    }
     __syncthreads();
-    float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += s_ss[w];
-    const float inv = 1.f / sqrtf(tot / (float)P.d + kStackEps);
-    for (int i = threadIdx.x; i < npc; i += kWG) {
-      float v[8];
-      norm_piece(P, rf, rb, t, i, v);
-      u32x4_t q;
-      q.x = bf16_rne(v[0] * inv) | (bf16_rne(v[1] * inv) << 16);
-      q.y = bf16_rne(v[2] * inv) | (bf16_rne(v[3] * inv) << 16);
-      q.z = bf16_rne(v[4] * inv) | (bf16_rne(v[5] * inv) << 16);
-      q.w = bf16_rne(v[6] * inv) | (bf16_rne(v[7] * inv) << 16);
-      if (xs != nullptr) xs[(size_t)(t - t0) * 4 * NCH + (i % 4) * NCH + i / 4] = q;
-      if (xg != nullptr) *reinterpret_cast<u32x4_t*>(xg + (size_t)t * P.d + 8 * i) = q;
+    for (int r = 0; r < kNormRows; ++r) {
+      if (r < ng) {  // uniform
+        const int t = g0 + r;
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += s_ss[r][w];
+        const float inv = 1.f / sqrtf(tot / (float)P.d + kStackEps);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 0 ? h0 : h1) {
+            const int i = h == 0 ? i0 : i1;
+            u32x4_t q;
+            q.x = bf16_rne(v[r][h][0] * inv) | (bf16_rne(v[r][h][1] * inv) << 16);
+            q.y = bf16_rne(v[r][h][2] * inv) | (bf16_rne(v[r][h][3] * inv) << 16);
+            q.z = bf16_rne(v[r][h][4] * inv) | (bf16_rne(v[r][h][5] * inv) << 16);
+            q.w = bf16_rne(v[r][h][6] * inv) | (bf16_rne(v[r][h][7] * inv) << 16);
+            if (xs != nullptr) xs[(size_t)(t - t0) * 4 * NCH + (i % 4) * NCH + i / 4] = q;
+            if (xg != nullptr) *reinterpret_cast<u32x4_t*>(xg + (size_t)t * P.d + 8 * i) = q;
+          }
+        }
+      }
     }
-    __syncthreads();  // s_ss is reused by the next row
+    __syncthreads();  // s_ss is reused by the next group
   }
 }
 
@@ -2162,13 +2187,18 @@ __global__ void __launch_bounds__(kWG) k_norm(Params P) {
 // pipeline stays on the GPU, no return to the host between operators;
 // [P5-TRT]: MoE gate then expert compute, per layer).  Layer l runs under tag
 // t0 + l.  Between layers every workgroup publishes its part of the stream r
-// (the combine's write-through stores; each wave waits for them to complete),
-// then its arrival word (hdr[kStarted + wg]) takes the next layer's tag.  The
-// next layer's router needs the input of every token, so each workgroup waits
-// until every arrival word has reached that tag, then acquires (which drops
-// its CU's and XCD's cached lines) and normalises r into LDS itself (every
-// workgroup gets the same bits, see norm_rows).  The router's first weight
-// loads are already in flight during that wait.
+// (the combine's stores, agent-scope atomics that write through the L2; each
+// wave waits for them to complete, so no L2 write-back is needed: one per wave
+// cost ~45 us per layer), then its arrival word (hdr[kStarted + wg]) takes
+// the next layer's tag.  The next layer's router needs the input of every
+// token, so each workgroup waits until every arrival word has reached that
+// tag, acquires (dropping its CU's and XCD's stale lines) and normalises r
+// into its LDS itself (every workgroup gets the same bits, see norm_rows).
+// The router's first weight loads are already in flight during the wait.
+// Measured on MI355X (8 verify-block layers): one launch 278 us per layer,
+// one launch per operator 265 us: back-to-back launches on one stream leave
+// no measurable gap between kernels, and this kernel's layer loop costs
+// registers (its hot loops reload some spilled values from scratch).
 
 // Tags of this launch lie in [t0, t0 + nl): a raised abort word in that range
 // stops the stack.
@@ -2429,7 +2459,7 @@ static DeviceInfo g_info[64];
 
 static const void* layer_kernel(int v, int mm) {
   switch (v) {
-    case kVAll: return mm == 1 ? (const void*)k_layer<kVAll, 1> : (const void*)k_layer<kVAll, 2>;
+    case kVAll: return (const void*)k_layer<kVAll, 2>;    // mm 2 only: mm 1 takes kVAllH (plan_launch)
     case kVAllH: return (const void*)k_layer<kVAllH, 1>;  // the static down path (mm 2) stages nothing
     case kVPairs: return mm == 1 ? (const void*)k_layer<kVPairs, 1> : (const void*)k_layer<kVPairs, 2>;
     default: return mm == 1 ? (const void*)k_layer<kVMfma, 1> : (const void*)k_layer<kVMfma, 2>;
@@ -2439,7 +2469,8 @@ static const void* layer_kernel(int v, int mm) {
 // The one-launch stack: small-batch path with x of every token in LDS.
 static const void* stack_kernel(int v, int mm) {
   if (v == kVAllH) return (const void*)k_stack<kVAllH, 1>;
-  if (v == kVAll) return mm == 1 ? (const void*)k_stack<kVAll, 1> : (const void*)k_stack<kVAll, 2>;
+  if (v == kVAll) return (const void*)k_stack<kVAll, 2>;
+  (void)mm;
   return nullptr;
 }
 
@@ -2452,10 +2483,9 @@ static int device_info(DeviceInfo* out) {
     int cus = 0, khz = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_EDEVICE;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_EDEVICE;
-    const void* ks[] = {layer_kernel(kVAll, 1), layer_kernel(kVAll, 2), layer_kernel(kVAllH, 1),
+    const void* ks[] = {layer_kernel(kVAll, 2), layer_kernel(kVAllH, 1),
                         layer_kernel(kVPairs, 1), layer_kernel(kVPairs, 2), layer_kernel(kVMfma, 1),
-                        layer_kernel(kVMfma, 2), stack_kernel(kVAll, 1), stack_kernel(kVAll, 2),
-                        stack_kernel(kVAllH, 1),
+                        layer_kernel(kVMfma, 2), stack_kernel(kVAll, 2), stack_kernel(kVAllH, 1),
                         (const void*)k_st_perm, (const void*)k_st_gate_up<true>, (const void*)k_st_gate_up<false>,
                         (const void*)k_st_down<0>, (const void*)k_st_down<1>, (const void*)k_st_down<2>};
     for (const void* f : ks) {
@@ -2568,9 +2598,13 @@ static int plan_launch(const moe_mxfp4_dims* dm, int32_t k, Launch* L) {
   }
   L->mm = chunks_per_lane_down(dm);
   if (L->mm < 1 || L->mm > 2) return MOE_ESHAPE;
-  // one or two tokens: few down units per workgroup, the h is best staged once
-  // per workgroup (kVAllH)
-  L->v = !L->small ? kVMfma : L->xmode == 1 ? kVPairs : (dm->T <= 2 && L->mm == 1) ? kVAllH : kVAll;
+  // x of every token in LDS: with one W_down chunk per lane the down step may
+  // stage h per workgroup (kVAllH), which pays where an expert has more than
+  // two tokens (the waves would reload h per pass: measured 320 instead of
+  // 240 us for a verify block with one 3-token expert) or a workgroup has few
+  // down units; otherwise it costs ~1% (verify, at most 2 tokens per expert:
+  // 249 instead of 247 us)
+  L->v = !L->small ? kVMfma : L->xmode == 1 ? kVPairs : L->mm == 1 ? kVAllH : kVAll;
   const LdsPlan pl = lds_plan(dm->T, dm->d, dm->E, k, L->xrows);
   if (pl.total > (size_t)kLdsMax) return MOE_ESHAPE;
   L->lds = pl.total;
@@ -2815,7 +2849,7 @@ int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const v
   P.pk_stride = (size_t)dims->E * moe_mxfp4_expert_packed_bytes(dims->d, dims->ffn);
   P.sc_stride = (size_t)dims->E * moe_mxfp4_expert_scale_bytes(dims->d, dims->ffn);
   hipStream_t s = (hipStream_t)stream;
-  if (sk && !(flags & MOE_LAYERS_PER_LAUNCH)) {
+  if (flags & MOE_LAYERS_ONE_LAUNCH) {
     P.nlayers = layers;
     void* args[] = {&P};
     const int grid = grid_for(di, sk, L.lds, 0);

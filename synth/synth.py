@@ -30,7 +30,7 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _SEEDS_PATH = os.path.join(os.path.dirname(_HERE), "tests", "golden", "seeds.json")
 
 # Stream ids of the tensors (see gen.c: synth_stream_key).
-TENSOR_X, TENSOR_WR, TENSOR_ZIPF = 0, 1, 5
+TENSOR_X, TENSOR_WR, TENSOR_ZIPF, TENSOR_XSHARED = 0, 1, 5, 6
 
 
 @dataclass(frozen=True)
@@ -45,6 +45,7 @@ class Config:
     k: int
     zipf_s: Optional[float] = None  # Zipf exponent of expert popularity, None = unbiased
     zipf_beta: float = 0.0  # logit bias strength: b_e = -beta * s * ln(rank_e)
+    x_shared: float = 0.0  # share of each token's variance in a component common to all tokens
     seed: int = 0  # base seed (expert weights)
     route_seed: int = 0  # seed of activations / router weights
     x_std: float = 1.0
@@ -67,6 +68,9 @@ _BASE = {
     "sweep_T16": Config("sweep_T16", T=16, d=7168, F=2048, E=256, k=8),
     "sweep_T22": Config("sweep_T22", T=22, d=7168, F=2048, E=256, k=8),
     "sweep_T32": Config("sweep_T32", T=32, d=7168, F=2048, E=256, k=8),
+    # a verify block of consecutive positions: the tokens share 70% of their
+    # variance, so they overlap in their experts (30 active, up to 7 tokens)
+    "verify_shared": Config("verify_shared", T=8, d=7168, F=2048, E=256, k=8, x_shared=0.7),
 }
 
 
@@ -204,10 +208,17 @@ def zipf_bias(cfg: Config, beta: Optional[float] = None) -> np.ndarray:
 def routing_inputs(cfg: Config, beta: Optional[float] = None):
     """(x bf16 bits uint16 [T, d], router weights fp32 [E, d]).
 
+    With x_shared = s > 0, every token is sqrt(s) c + sqrt(1 - s) n_t with one
+    common normal vector c (stream TENSOR_XSHARED) and its own n_t.
     With a Zipf workload, column 0 carries the popularity bias: x[:, 0] = 1
     and W_r[:, 0] = b_e, so every token's logit for expert e gains b_e.
     """
     x32 = normals(cfg.route_seed, TENSOR_X, 0, cfg.T * cfg.d, cfg.x_std).reshape(cfg.T, cfg.d)
+    if cfg.x_shared > 0:
+        # x_t = sqrt(s) c + sqrt(1 - s) n_t: common c, own n_t, same variance
+        c = normals(cfg.route_seed, TENSOR_XSHARED, 0, cfg.d, cfg.x_std)
+        x32 = (np.float32(math.sqrt(cfg.x_shared)) * c[None, :]
+               + np.float32(math.sqrt(1.0 - cfg.x_shared)) * x32).astype(np.float32)
     wr = normals(cfg.route_seed, TENSOR_WR, 0, cfg.E * cfg.d, cfg.wr_std).reshape(cfg.E, cfg.d)
     if cfg.zipf_s is not None:
         x32[:, 0] = 1.0

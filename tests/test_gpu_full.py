@@ -2,7 +2,9 @@
 top-8), in the launch configuration the benchmark times (the persistent
 single launch with its default grid).
 
-decode (T=1) and verify (T=8): every output element against the oracle.
+decode (T=1), verify (T=8) and verify_shared (T=8 tokens sharing most of
+their variance, so up to 7 tokens per expert): every output element against
+the oracle.
 batched_verify (T=128, Zipf-skewed routing) and dense (T=512): routing and
 permutation for all tokens, outputs for a sample of tokens (the oracle runs
 only those tokens' expert pairs).  The verify-block sweep (T = 4, 16, 22, 32)
@@ -72,6 +74,13 @@ def test_decode_T1(full_env):
 
 def test_verify_T8(full_env):
     _run(full_env, "verify")
+
+
+def test_verify_shared_T8(full_env):
+    """Verify block whose tokens share most of their variance: 30 experts, up
+    to 7 tokens each (the down step stages h per workgroup)."""
+    got, ref = _run(full_env, "verify_shared")
+    assert np.diff(ref.offsets).max() >= 5
 
 
 def test_batched_verify_T128_zipf(full_env):
