@@ -87,7 +87,7 @@ constexpr int kGUPass = 32;            // tokens per gate/up pass (2 groups of 1
 constexpr int kDnPass = 32;            // tokens per down pass (2 groups of 16)
 constexpr int kTileRow = 272;          // LDS bytes per token row of an activation tile (256 + 16 pad)
 constexpr int kGUK = 4;                // gate/up K blocks per step (8 KiB of codes per wave)
-constexpr int kDnK = 1;                // down K blocks per step (4 KiB of codes per wave)
+constexpr int kDnK = 2;                // down K blocks per step (8 KiB of codes per wave: whole 128-byte lines)
 constexpr int kGUUnitRows = kWaves * 16;             // 128 row pairs
 constexpr int kDnUnitRows = kWaves * kDnTiles * 16;  // 512 rows
 constexpr size_t kMfmaLds = 2 * (size_t)kGUK * kGUPass * kTileRow;  // two activation tiles of a step
@@ -1597,29 +1597,66 @@ struct GUA {
   uint32_t keep;                // bit b: K block b's chunk is in range
 };
 
-// This wave's tile of step c: rows (u % R) * 128 + 16 * wave + l % 16 of
-// W_gate and W_up, chunks 4(kGUK j + b) + l / 16.  Rows past F (last unit of
-// an expert) and chunks past d read a valid chunk and get a zero scale at use.
-// Nothing is computed from the loaded data here, so the loads stay in flight.
+// This wave's tile of step c: rows r0 .. r0 + 15 (r0 = (u % R) * 128 + 16 *
+// wave) of W_gate and W_up, chunks 16 j .. 16 j + 15 (kGUK = 4 K blocks of 4
+// chunks).  The loads read whole 128-byte lines: load i takes rows
+// r0 + 8 (i & 1) + l / 8, chunks 16 j + 8 (i >> 1) + l % 8 (eight lanes per
+// row).  The MFMA layout wants lane l to hold row r0 + l % 16, chunk
+// 16 j + 4 b + l / 16 for K block b, i.e. four 64-byte pieces per row spread
+// over four loads; loads of that shape moved the same bytes in half-lines and
+// made the T=512 layer 25% slower (2.58 instead of 2.07 ms).  gu_mfma_take
+// moves the data into the MFMA layout when it is used.  Rows past F (last
+// unit of an expert) and chunks past d read a valid chunk and get a zero scale
+// at use.  Nothing is computed from the loaded data here, so the loads stay in
+// flight.
 __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int R, GUA& A) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = d / 32;
-  const int row = (c.u % R) * kGUUnitRows + 16 * wave + (lane & 15);
-  const int rr = min(row, F - 1);
+  const int r0 = (c.u % R) * kGUUnitRows + 16 * wave;
   const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
-  const uint8_t* pg = P.packed + (size_t)c.e * pbytes + (size_t)rr * (d / 2);
-  const uint8_t* sg = P.scales + (size_t)c.e * sbytes + (size_t)rr * NCH;
+  const uint8_t* pe = P.packed + (size_t)c.e * pbytes;
+  const uint8_t* se = P.scales + (size_t)c.e * sbytes;
   A.keep = 0;
 #pragma unroll
-  for (int b = 0; b < kGUK; ++b) {
-    const int ch = 4 * (c.j * kGUK + b) + (lane >> 4);
-    const int cc = min(ch, NCH - 1);
-    A.g[b] = ld_stream16(pg + (size_t)cc * 16);
-    A.u[b] = ld_stream16(pg + (size_t)F * d / 2 + (size_t)cc * 16);
-    A.sg[b] = sg[cc];
-    A.su[b] = sg[(size_t)F * NCH + cc];
-    A.keep |= (row < F && ch < NCH) ? 1u << b : 0u;
+  for (int i = 0; i < kGUK; ++i) {
+    const int rr = min(r0 + 8 * (i & 1) + (lane >> 3), F - 1);
+    const int cc = min(16 * c.j + 8 * (i >> 1) + (lane & 7), NCH - 1);
+    A.g[i] = ld_stream16(pe + (size_t)rr * (d / 2) + (size_t)cc * 16);
+    A.u[i] = ld_stream16(pe + (size_t)F * d / 2 + (size_t)rr * (d / 2) + (size_t)cc * 16);
+    A.sg[i] = se[(size_t)rr * NCH + cc];
+    A.su[i] = se[(size_t)F * NCH + (size_t)rr * NCH + cc];
+    // in range, for the MFMA-layout chunk this lane will hold for block i
+    const int row = r0 + (lane & 15), ch = 16 * c.j + 4 * i + (lane >> 4);
+    A.keep |= (row < F && ch < NCH) ? 1u << i : 0u;
   }
+}
+// K block b of the MFMA layout from the loads: lane l = 16 h + r takes chunk
+// 4 b + h of row r, held by load 2 (b >> 1) + (r >> 3) of lane
+// 8 (r & 7) + 4 (b & 1) + h.
+__device__ __forceinline__ uint32_t bperm(uint32_t v, int addr) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
+}
+__device__ __forceinline__ void gu_mfma_take(const GUA& A, int b, u32x4_t& g, u32x4_t& u, uint32_t& sg,
+                                             uint32_t& su) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, h = lane >> 4;
+  const int addr = 4 * (8 * (r & 7) + 4 * (b & 1) + h);
+  const bool hi = r >= 8;
+  const int i0 = 2 * (b >> 1), i1 = i0 + 1;
+  const auto pick = [&](uint32_t a0, uint32_t a1) {
+    const uint32_t v0 = bperm(a0, addr), v1 = bperm(a1, addr);
+    return hi ? v1 : v0;
+  };
+  g.x = pick(A.g[i0].x, A.g[i1].x);
+  g.y = pick(A.g[i0].y, A.g[i1].y);
+  g.z = pick(A.g[i0].z, A.g[i1].z);
+  g.w = pick(A.g[i0].w, A.g[i1].w);
+  u.x = pick(A.u[i0].x, A.u[i1].x);
+  u.y = pick(A.u[i0].y, A.u[i1].y);
+  u.z = pick(A.u[i0].z, A.u[i1].z);
+  u.w = pick(A.u[i0].w, A.u[i1].w);
+  sg = pick(A.sg[i0], A.sg[i1]);
+  su = pick(A.su[i0], A.su[i1]);
 }
 
 // x tile of step c: token rows n < 32 of the pass, K blocks kGUK j .. +kGUK,
@@ -1670,9 +1707,12 @@ __device__ __forceinline__ void gu_mfma_step(const GUA& A, const char* tile, f32
       for (int g = 0; g < NG; ++g)
         x[s][g] = *reinterpret_cast<const bf16x8_t*>(b0 + (b * kGUPass + g * 16) * kTileRow + s * 16);
     const bool in = (A.keep >> b) & 1u;
+    u32x4_t cg, cu;
+    uint32_t sgb, sub;
+    gu_mfma_take(A, b, cg, cu, sgb, sub);
     bf16x8_t wg[4], wu[4];
-    decode_chunk_a(A.g[b], e8m0_to_f32(in ? A.sg[b] : 0u), wg);
-    decode_chunk_a(A.u[b], e8m0_to_f32(in ? A.su[b] : 0u), wu);
+    decode_chunk_a(cg, e8m0_to_f32(in ? sgb : 0u), wg);
+    decode_chunk_a(cu, e8m0_to_f32(in ? sub : 0u), wu);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -1758,33 +1798,57 @@ __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uin
 
 // ---- down ----
 struct DnA {
-  u32x4_t w[kDnK][kDnTiles];
-  uint32_t s[kDnK][kDnTiles];  // scale bytes as loaded
-  uint32_t keep;               // bit b * kDnTiles + t: in range
+  u32x4_t w[kDnK * kDnTiles];  // as loaded (load i)
+  uint32_t s[kDnK * kDnTiles]; // scale bytes as loaded
+  uint32_t keep;               // bit b * kDnTiles + t: the MFMA-layout chunk of tile t, block b is in range
 };
+static_assert(kDnK == 2, "a step covers one 128-byte line (8 chunks) of each W_down row");
 
-// This wave's 4 tiles of step c: rows (u % R) * 512 + 64 * wave + 16t + l % 16
-// of W_down, chunks 4(kDnK j + b) + l / 16 (K = F).
+// This wave's 4 tiles of step c: rows r0 .. r0 + 63 (r0 = (u % R) * 512 +
+// 64 * wave) of W_down, chunks 8 j .. 8 j + 7 (K = F): one 128-byte line per
+// row.  Load i takes rows r0 + 8 i + l / 8, chunk 8 j + l % 8 (whole lines; see
+// gu_mfma_load); dn_mfma_take moves tile t, block b into the MFMA layout
+// (lane l: row r0 + 16 t + l % 16, chunk 8 j + 4 b + l / 16).
 __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int R, DnA& A) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = F / 32;
   const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
   const uint8_t* pd = P.packed + (size_t)c.e * pbytes + (size_t)F * d;
   const uint8_t* sd = P.scales + (size_t)c.e * sbytes + (size_t)F * d / 16;
+  const int r0 = (c.u % R) * kDnUnitRows + 64 * wave;
   A.keep = 0;
 #pragma unroll
-  for (int b = 0; b < kDnK; ++b) {
-    const int ch = 4 * (c.j * kDnK + b) + (lane >> 4);
-    const int cc = min(ch, NCH - 1);
+  for (int i = 0; i < kDnK * kDnTiles; ++i) {
+    const int rr = min(r0 + 8 * i + (lane >> 3), d - 1);
+    const int cc = min(8 * c.j + (lane & 7), NCH - 1);
+    A.w[i] = ld_stream16(pd + (size_t)rr * (F / 2) + (size_t)cc * 16);
+    A.s[i] = sd[(size_t)rr * NCH + cc];
+  }
+#pragma unroll
+  for (int b = 0; b < kDnK; ++b)
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
-      const int row = (c.u % R) * kDnUnitRows + 64 * wave + 16 * t + (lane & 15);
-      const int rr = min(row, d - 1);
-      A.w[b][t] = ld_stream16(pd + (size_t)rr * (F / 2) + (size_t)cc * 16);
-      A.s[b][t] = sd[(size_t)rr * NCH + cc];
+      const int row = r0 + 16 * t + (lane & 15), ch = 8 * c.j + 4 * b + (lane >> 4);
       A.keep |= (row < d && ch < NCH) ? 1u << (b * kDnTiles + t) : 0u;
     }
-  }
+}
+// Tile t, block b in the MFMA layout: lane l = 16 h + r takes row 16 t + r,
+// chunk 4 b + h, held by load 2 t + (r >> 3) of lane 8 (r & 7) + 4 b + h.
+__device__ __forceinline__ void dn_mfma_take(const DnA& A, int b, int t, u32x4_t& w, uint32_t& sc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, h = lane >> 4;
+  const int addr = 4 * (8 * (r & 7) + 4 * b + h);
+  const bool hi = r >= 8;
+  const int i0 = 2 * t, i1 = i0 + 1;
+  const auto pick = [&](uint32_t a0, uint32_t a1) {
+    const uint32_t v0 = bperm(a0, addr), v1 = bperm(a1, addr);
+    return hi ? v1 : v0;
+  };
+  w.x = pick(A.w[i0].x, A.w[i1].x);
+  w.y = pick(A.w[i0].y, A.w[i1].y);
+  w.z = pick(A.w[i0].z, A.w[i1].z);
+  w.w = pick(A.w[i0].w, A.w[i1].w);
+  sc = pick(A.s[i0], A.s[i1]);
 }
 
 // h tile of step c: pairs n < 32 of the pass, values 128(kDnK j) .. +128 kDnK
@@ -1862,8 +1926,13 @@ __device__ __forceinline__ void dn_mfma_step(const DnA& A, const char* hi_tile, 
 #pragma unroll
   for (int b = 0; b < kDnK; ++b) {
     float sc[kDnTiles];
+    u32x4_t wt[kDnTiles];
 #pragma unroll
-    for (int t = 0; t < kDnTiles; ++t) sc[t] = e8m0_to_f32((A.keep >> (b * kDnTiles + t)) & 1u ? A.s[b][t] : 0u);
+    for (int t = 0; t < kDnTiles; ++t) {
+      uint32_t sb;
+      dn_mfma_take(A, b, t, wt[t], sb);
+      sc[t] = e8m0_to_f32((A.keep >> (b * kDnTiles + t)) & 1u ? sb : 0u);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t bh[NG], bl[NG];
@@ -1875,7 +1944,7 @@ __device__ __forceinline__ void dn_mfma_step(const DnA& A, const char* hi_tile, 
       }
       bf16x8_t a[kDnTiles];
 #pragma unroll
-      for (int t = 0; t < kDnTiles; ++t) a[t] = decode_op_a(A.w[b][t], sc[t], s);
+      for (int t = 0; t < kDnTiles; ++t) a[t] = decode_op_a(wt[t], sc[t], s);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
 #pragma unroll
