@@ -322,6 +322,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Two tagged words {v0, tag, v1, tag} with one 16-byte store that writes
+// through the L2 (sc1, the cache policy of st_tagged's 8-byte atomic stores).
+// An aligned 16-byte store reaches memory in one piece, so readers (16-byte
+// coherent loads, each 8-byte half read whole) never see half a word; the
+// stores of neighbouring lanes then fill whole 128-byte lines instead of
+// 8-byte pieces of them.
+__device__ __forceinline__ void st_tagged2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t v0, uint32_t v1,
+                                           uint32_t tag) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v0, tag, v1, tag}, r, byte_off, 0, 16);
+}
+
 // 16-byte agent-coherent load (sc1: not served from a stale L2 line of
 // another call) of two tagged words {lo value, lo tag, hi value, hi tag}.
 // Each aligned 8-byte half is read single-copy atomically.  Unlike atomic

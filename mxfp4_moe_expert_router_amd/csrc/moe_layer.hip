@@ -122,6 +122,7 @@ struct Params {
   int mfma;           // 1: x does not fit in LDS, expert steps on MFMA
   int xmode;          // small-batch path: 0 x of every token in LDS, 1 x of the workgroup's pairs (see stage_pairs)
   int xrows;          // small-batch path: rows of x the LDS holds
+  int narrow;         // 1: every byte offset into hq and yq fits in 32 bits (16-byte tagged stores)
   // A stack of layers on one residual stream r (r_0 = x0, x_l =
   // bf16(rmsnorm(r_l)), r_{l+1} = r_l + layer_l(x_l), out = r_L): the combine
   // adds the layer's output to r, which out holds.
@@ -1730,13 +1731,22 @@ __device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int np = min(kGUPass, c.ne - c.pass);
   const int row0 = (c.u % R) * kGUUnitRows + 16 * wave;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq, (uint32_t)((size_t)P.T * P.k * P.F * 8));
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int n = 16 * g + (lane & 15);
     if (row0 < P.F && n < np) {
-      uint64_t* hp = P.hq + (size_t)(c.p0 + c.pass + n) * P.F + row0 + 4 * (lane >> 4);
+      const size_t w0 = (size_t)(c.p0 + c.pass + n) * P.F + row0 + 4 * (lane >> 4);
+      uint32_t hb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_tagged(hp + i, __builtin_bit_cast(uint32_t, swiglu(ag[g][i], au[g][i])), tag);
+      for (int i = 0; i < 4; ++i) hb[i] = __builtin_bit_cast(uint32_t, swiglu(ag[g][i], au[g][i]));
+      if (P.narrow) {  // uniform
+        st_tagged2(rs, (uint32_t)(w0 * 8), hb[0], hb[1], tag);
+        st_tagged2(rs, (uint32_t)(w0 * 8 + 16), hb[2], hb[3], tag);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_tagged(P.hq + w0 + i, hb[i], tag);
+      }
     }
     ag[g] = au[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -1963,6 +1973,7 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
                                               f32x4_t (&acc)[kDnTiles][2]) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int np = min(kDnPass, c.ne - c.pass);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.yq, (uint32_t)((size_t)P.T * P.k * P.d * 8));
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int n = 16 * g + (lane & 15);
@@ -1972,9 +1983,17 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
     for (int t = 0; t < kDnTiles; ++t) {
       const int row0 = (c.u % R) * kDnUnitRows + 64 * wave + 16 * t;
       if (row0 < P.d && n < np) {
-        uint64_t* yp = P.yq + (size_t)slot * P.d + row0 + 4 * (lane >> 4);
+        const size_t w0 = (size_t)slot * P.d + row0 + 4 * (lane >> 4);
+        uint32_t yb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st_tagged(yp + i, __builtin_bit_cast(uint32_t, gate * acc[t][g][i]), tag);
+        for (int i = 0; i < 4; ++i) yb[i] = __builtin_bit_cast(uint32_t, gate * acc[t][g][i]);
+        if (P.narrow) {  // uniform
+          st_tagged2(rs, (uint32_t)(w0 * 8), yb[0], yb[1], tag);
+          st_tagged2(rs, (uint32_t)(w0 * 8 + 16), yb[2], yb[3], tag);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st_tagged(P.yq + w0 + i, yb[i], tag);
+        }
       }
       acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -2614,6 +2633,7 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.mfma = 0;
   P.xmode = 0;
   P.xrows = 0;
+  P.narrow = (size_t)dm->T * k * (size_t)(dm->d > dm->ffn ? dm->d : dm->ffn) * 8 < ((size_t)1 << 32) ? 1 : 0;
   P.stack_layers = 0;
   P.layer0 = 0;
   P.nlayers = 1;
