@@ -12,13 +12,15 @@
 //
 // Layout of the work: a wave quantizes 16 blocks at a time, every load
 // instruction reading 1 KiB of contiguous input (see k_quantize); a block's
-// maximum comes from lane exchanges within its lane group.  Every decision is taken on the fp32 bit patterns
-// with integer operations: for values >= 0 the order of the patterns is the
-// order of the values (subnormals included), and each decision point
-// t 2^X (t = 0.25, 0.75, ..., 5: at most three significant bits) is an exact
-// fp32 value whose pattern is built with shifts, so the codes are exact and
-// do not depend on how the hardware treats subnormal arithmetic.  HBM-bound:
-// 4.5 bytes per element (fp32 in) or 2.5 (bf16 in).
+// maximum comes from lane exchanges within its lane group.  The shared
+// exponent is taken from the fp32 bit pattern of the maximum with integer
+// operations.  The codes come from the hardware's scaled E2M1 convert, two
+// per instruction, for every block whose X is at least -120; below that
+// (blocks of values under 2^-118) they come from comparisons of the fp32 bit
+// patterns with the decision points t 2^X (t = 0.25, 0.75, ..., 5: at most
+// three significant bits, exact fp32 values built with shifts), which do not
+// depend on how the hardware treats subnormal operands.  HBM-bound: 4.5 bytes
+// per element (fp32 in) or 2.5 (bf16 in).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,48 +48,89 @@ __device__ __forceinline__ int ilog2_bits(uint32_t a) {
   return (31 - __builtin_clz(a)) - 149;  // subnormal
 }
 
+// Smallest shared exponent for which the hardware convert below is taken.
+// From 2^-120 up, the scale 2^X is a normal fp32 value, and every element
+// that can round to a nonzero code (|v| >= 2^(X-2) >= 2^-122) is normal too,
+// so the convert sees exact operands; blocks below it take the bit-pattern
+// comparisons.
+constexpr int kHwMinX = -120;
+
+// Two E2M1 codes of v0 / sc and v1 / sc (sc a power of two) into byte i of
+// word (v0 in the low nibble); the byte index must be a literal.
+__device__ __forceinline__ uint32_t cvt_pair_fp4(uint32_t word, float v0, float v1, float sc, int i) {
+  switch (i) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v0, v1, sc, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v0, v1, sc, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v0, v1, sc, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v0, v1, sc, 3);
+  }
+}
+
 // The codes of one block from its elements' patterns: every lane of the
 // block's lane group holds N of them; the group (G lanes, aligned) exchanges
 // its maximum.  Returns the lane's N codes packed (element 0 in the low
 // nibble) and the block's X.
+//
+// Common case: gfx950's scaled convert (v_cvt_scalef32_pk_fp4_f32) turns two
+// fp32 values into two E2M1 codes in one instruction.  It divides by the
+// scale's power of two (exact here), rounds to the nearest E2M1 value with
+// ties to the even mantissa bit, saturates at 6 and copies the sign bit, so
+// it gives exactly the rule above except for a negative zero (sign bit set,
+// where the rule sets it only for v < 0): a negative zero is passed as +0.
 template <int N, int G>
 __device__ __forceinline__ uint32_t block_codes(const uint32_t (&u)[N], int& Xout) {
+  static_assert(N % 2 == 0 && N <= 8, "pairs of elements, one byte of codes each");
+  uint32_t a[N];
   uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < N; ++i) amax = max(amax, u[i] & 0x7FFFFFFFu);
+  for (int i = 0; i < N; ++i) {
+    a[i] = u[i] & 0x7FFFFFFFu;
+    amax = max(amax, a[i]);
+  }
 #pragma unroll
   for (int o = 1; o < G; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
   const int X = amax ? min(max(ilog2_bits(amax) - 2, -127), 127) : -127;
+  Xout = X;
+  uint32_t word = 0;
+  if (X >= kHwMinX) {
+    const float sc = __uint_as_float((uint32_t)(X + 127) << 23);
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float v0 = __uint_as_float(a[2 * i] ? u[2 * i] : 0u);
+      const float v1 = __uint_as_float(a[2 * i + 1] ? u[2 * i + 1] : 0u);
+      word = cvt_pair_fp4(word, v0, v1, sc, i);
+    }
+    return word;
+  }
   // decision points t 2^X, t = 1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5; at a tie the
   // even mantissa bit wins: strictly above for 1/4, 5/4, 5/2, 5 and at or
   // above for 3/4, 7/4, 7/2
   const uint32_t d0 = f32_bits_of(1, X - 2), d1 = f32_bits_of(3, X - 2), d2 = f32_bits_of(5, X - 2),
                  d3 = f32_bits_of(7, X - 2), d4 = f32_bits_of(5, X - 1), d5 = f32_bits_of(7, X - 1),
                  d6 = f32_bits_of(5, X);
-  uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const uint32_t a = u[i] & 0x7FFFFFFFu;
-    const uint32_t code = (uint32_t)(a > d0) + (uint32_t)(a >= d1) + (uint32_t)(a > d2) + (uint32_t)(a >= d3) +
-                          (uint32_t)(a > d4) + (uint32_t)(a >= d5) + (uint32_t)(a > d6);
+    const uint32_t code = (uint32_t)(a[i] > d0) + (uint32_t)(a[i] >= d1) + (uint32_t)(a[i] > d2) +
+                          (uint32_t)(a[i] >= d3) + (uint32_t)(a[i] > d4) + (uint32_t)(a[i] >= d5) +
+                          (uint32_t)(a[i] > d6);
     // sign bit for v < 0 (a negative zero keeps code 0 without it)
-    word |= (code | ((u[i] >> 31) && a ? 8u : 0u)) << (4 * i);
+    word |= (code | ((u[i] >> 31) && a[i] ? 8u : 0u)) << (4 * i);
   }
-  Xout = X;
   return word;
 }
 
 // A wave takes 16 blocks at a time, kU chunks of them per round with all
-// the round's loads issued first.  fp32: two 1 KiB loads per chunk, lane l
-// holding elements 4l..4l+3 of each half (8 lanes per block); bf16: one 1 KiB
-// load, lane l holding elements 8l..8l+7 (4 lanes per block).  Every load
+// the round's loads issued first (kU = 4 for fp32, 2 for bf16: the fastest
+// measured on MI355X).  fp32: two 1 KiB loads per chunk, lane l holding
+// elements 4l..4l+3 of each half (8 lanes per block); bf16: one 1 KiB load,
+// lane l holding elements 8l..8l+7 (4 lanes per block).  Every load
 // instruction reads 1 KiB of contiguous input; chunks past the end re-read
 // the last chunk (in bounds) and store nothing.
-constexpr int kU = 4;
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) k_quantize(const void* w, int64_t nblocks, uint8_t* packed,
                                                        uint8_t* scales) {
   constexpr int kH = BF16 ? 1 : 2;  // 1 KiB loads per chunk
+  constexpr int kU = BF16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
@@ -157,9 +200,19 @@ extern "C" int moe_mxfp4_quantize(const void* w, int32_t dtype, int64_t rows, in
     (void)hipGetLastError();
     return MOE_EDEVICE;
   }
-  // enough workgroups to fill the CUs several times over, at most one chunk of 16 blocks per wave
+  // at most one chunk of 16 blocks per wave, and no more workgroups than the
+  // CUs hold at once: every workgroup then runs from the start to the end,
+  // with no second, partly filled wave of workgroups at the tail
+  const void* kern = dtype == MOE_QDTYPE_BF16 ? (const void*)moe_q::k_quantize<true>
+                                              : (const void*)moe_q::k_quantize<false>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, moe_q::kThreads, 0) != hipSuccess ||
+      per_cu < 1) {
+    (void)hipGetLastError();
+    return MOE_EDEVICE;
+  }
   int64_t grid = ((nblocks + 15) / 16 + moe_q::kThreads / 64 - 1) / (moe_q::kThreads / 64);
-  const int64_t cap = (int64_t)cus * 16;
+  const int64_t cap = (int64_t)cus * per_cu;
   if (grid > cap) grid = cap;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == MOE_QDTYPE_BF16)

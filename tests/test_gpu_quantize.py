@@ -3,7 +3,7 @@ quantizer, bit for bit: codes and scale bytes.  The oracle quantizer itself is
 pinned in test_oracle_codec.py (round trips, RNE ties, saturation, error
 bound).  fp32 and bf16 inputs; ragged row counts; hand-built blocks at every
 E2M1 decision point (ties go to the even mantissa bit), saturation, zeros of
-both signs, fp32 subnormals and values near the fp32 maximum."""
+both signs, fp32 subnormals of both signs and values near the fp32 maximum."""
 import numpy as np
 import pytest
 
@@ -67,7 +67,9 @@ def test_decision_points_and_edges(env):
     # sit at, just below and just above every E2M1 decision point
     rows = []
     pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0]
-    for X in (-10, 0, 3):
+    # X from -126 (subnormal decision points) over -121 / -120 (either side of
+    # the smallest X the kernel hands to the hardware convert) to 3
+    for X in (-126, -121, -120, -10, 0, 3):
         for sgn in (1.0, -1.0):
             row = [6.0 * 2.0 ** X]
             for q in pts:
@@ -78,6 +80,8 @@ def test_decision_points_and_edges(env):
             rows.append(row[:64])
     rows.append([0.0] * 32 + [-0.0] * 32)                                 # zero blocks, both signs
     rows.append([1e-45 * (i % 3) for i in range(64)])                      # fp32 subnormals
+    rows.append([-1e-45 * (i % 3) for i in range(32)]                     # negative subnormals, alone
+                + [-3e-39 * (i % 5) for i in range(31)] + [2.0 ** -119])   # and under a normal maximum
     rows.append([3.0e38 * ((-1) ** i) for i in range(64)])                # near the fp32 maximum
     rows.append([7.0, -6.5] * 16 + [1.0] + [0.0] * 31)                    # saturation, a lone 1
     w = np.array(rows, dtype=np.float32)
