@@ -909,8 +909,12 @@ struct GURow {
 };
 
 // Loads are unconditional (no divergent branch between them, so they all stay
-// in flight): a lane past the end of the row re-reads the row's last chunk and
-// gets a zero scale, which decodes its codes to 0.
+// in flight): a lane past the end of the row re-reads the row's last chunk
+// with its scale byte masked to 0, i.e. 2^-127 (the convert takes the scale's
+// exponent; an fp32 0 is exponent 0).  Its 32 terms then add less than 2^-110
+// for |x| < 2^8, below half an ulp of any fp32 sum above 2^-86 in magnitude:
+// they do not change g or u.  (Zeroing the codes instead cost 2% of the
+// verify layer's time.)
 __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho, GURow& R) {
   const int lane = threadIdx.x & (kWave - 1);
   const int d = P.d, F = P.F, NCH = d / 32;
@@ -930,25 +934,6 @@ __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho,
     const uint32_t keep = c < NCH ? 0xFFu : 0u;
     R.sg[m] = sg[cc] & keep;
     R.su[m] = su[cc] & keep;
-  }
-}
-
-// x of token row `xrow` (piece-transposed in LDS) against a loaded row pair.
-__device__ __forceinline__ void gu_dot(const Params& P, const u32x4_t* xs, int xrow, const GURow& R, float& g,
-                                       float& u) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int NCH = P.d / 32;
-  const u32x4_t* xb = xs + (size_t)xrow * 4 * NCH;
-#pragma unroll
-  for (int m = 0; m < kGUChunks; ++m) {
-    if (kWave * m < NCH) {  // uniform
-      const int cc = min(lane + kWave * m, NCH - 1);
-      u32x4_t xq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xq[q] = xb[q * NCH + cc];
-      g = dot32_bf16(R.g[m], e8m0_to_f32(R.sg[m]), xq, g);
-      u = dot32_bf16(R.u[m], e8m0_to_f32(R.su[m]), xq, u);
-    }
   }
 }
 
@@ -981,7 +966,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
     }
 #pragma unroll
     for (int m = 0; m < kGUChunks; ++m) {
-      if (kWave * m < NCH) {  // uniform; lanes past the row end have scale 0
+      if (kWave * m < NCH) {  // uniform; lanes past the row end have scale byte 0 (gu_load)
         bf16x2_t dg[16], du[16];
         decode32_bf16(R.g[m], e8m0_to_f32(R.sg[m]), dg);
         decode32_bf16(R.u[m], e8m0_to_f32(R.su[m]), du);
@@ -1201,7 +1186,7 @@ __device__ __forceinline__ void dn_compute(const Params& P, const Smem& S, uint3
   for (int j = 0; j < ROWS; ++j) {
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-      if (kWave * m < NCH) {  // uniform; lanes past the row end have scale 0 and h 0
+      if (kWave * m < NCH) {  // uniform; lanes past the row end have h 0, so they add exactly 0
         float v[32];
         decode32_f32(R.w[j][m], e8m0_to_f32(R.s[j][m]), v);
 #pragma unroll
@@ -1296,8 +1281,9 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
   for (int tg = 0; tg < ne; tg += 2) {
     const int nt = min(2, ne - tg);
     if (HL) {
-      // lanes past the row's chunks read the last chunk's h: their codes have
-      // scale 0 (dn_load), so it contributes 0
+      // lanes past the row's chunks (F < 2048) read the last chunk's h; their
+      // codes have scale byte 0 (dn_load), 2^-127, which puts their terms far
+      // below the rounding of the sums (see gu_load)
       float hl[2][1][32];
       const int c = min(lane, P.F / 32 - 1);
 #pragma unroll
