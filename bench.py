@@ -51,6 +51,37 @@ def traffic_record(workload: str):
     return rec
 
 
+def stream_read_ref(dev, stream, gib: int = 4, reps: int = 10) -> dict:
+    """Plain streaming reads on the same GPU, outside the timed region: two of
+    torch's reductions over a gib-GiB buffer (each reads every byte once; of
+    the torch reductions tried on MI355X these were the fastest, ~6 TB/s,
+    where a plain fp32 sum reached ~4), each the mean of reps calls timed with
+    HIP events; the faster one is the reference.  What a read-only kernel
+    reaches on this machine, next to the 8 TB/s peak."""
+    import torch
+
+    buf = torch.ones(gib << 28, dtype=torch.float32, device=dev)
+    nbytes = buf.numel() * 4
+    best = None
+    for how, f in (("torch int64 sum", lambda: buf.view(torch.int64).sum()),
+                   ("torch fp32 column sums [8192, n]", lambda: buf.view(8192, -1).sum(dim=0))):
+        for _ in range(3):
+            f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        gbs = nbytes / (a.elapsed_time(b) * 1e-3 / reps) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, how)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GBs": round(best[0], 1), "how": f"{best[1]} over a {gib} GiB buffer, mean of {reps} (the faster of two)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +190,8 @@ def main():
         raise RuntimeError("device watchdog fired during the timed steps")
     launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
+    ref = stream_read_ref(dev, stream)
+
     it = moe.intermediates(ws, dims, cfg.k)
     n_active = int(it["n_active"].item())
     alg_bytes = synth.algorithmic_bytes(cfg, n_active)
@@ -214,6 +247,7 @@ def main():
                                                                    / MXFP4_PEAK_TFLOPS, 5),
         },
         "kernel_hash": kernel_hash(),
+        "stream_read_ref": dict(ref, layer_kernel_frac=round(kern_gbs / ref["GBs"], 4)),
     }
 
     if not args.no_cpu_baseline:
