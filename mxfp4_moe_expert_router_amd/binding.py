@@ -159,18 +159,29 @@ def dims_of(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor) -> La
     return LayerDims(int(T), int(d), int(ffn), int(E))
 
 
-def _validate(x, router_w, packed, scales, out):
-    for name, t, dt in (("x", x, torch.bfloat16), ("router_w", router_w, torch.float32),
-                        ("packed", packed, torch.uint8), ("scales", scales, torch.uint8),
-                        ("out", out, torch.float32)):
+def _validate(x, router_w, packed, scales, out, dims: Optional[LayerDims] = None, layers: int = 1):
+    """dtype, contiguity and (with dims) element counts of every tensor given,
+    then that each lives on the device: a short buffer would otherwise let a
+    kernel read or write past its end."""
+    want = {}
+    if dims is not None:
+        T, d, F, E = dims.T, dims.d, dims.ffn, dims.E
+        want = {"x": T * d, "router_w": layers * E * d, "packed": layers * E * 3 * d * F // 2,
+                "scales": layers * E * 3 * d * F // 32, "out": T * d}
+    named = (("x", x, torch.bfloat16), ("router_w", router_w, torch.float32), ("packed", packed, torch.uint8),
+             ("scales", scales, torch.uint8), ("out", out, torch.float32))
+    for name, t, dt in named:
         if t is None:
             continue
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
         if t.dtype != dt and not (name == "x" and t.dtype == torch.int16):
             raise ValueError(f"{name} must be {dt}, got {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if name in want and t.numel() != want[name]:
+            raise ValueError(f"{name} has {t.numel()} elements, the sizes need {want[name]}")
+    for name, t, _ in named:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
 
 
 def forward(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, topk: int,
@@ -181,7 +192,7 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor, scale
     dims = dims or dims_of(x, router_w, packed)
     if out is None:
         out = torch.empty((dims.T, dims.d), dtype=torch.float32, device=x.device)
-    _validate(x, router_w, packed, scales, out)
+    _validate(x, router_w, packed, scales, out, dims)
     if workspace is None:
         workspace = alloc_workspace(dims, topk, x.device)
     cd = dims.c()
@@ -220,7 +231,7 @@ def forward_layers(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor
     dims = dims or LayerDims(int(x.shape[0]), int(d), int(packed.shape[2] * 2 // (3 * d)), int(E))
     if out is None:
         out = torch.empty((dims.T, dims.d), dtype=torch.float32, device=x.device)
-    _validate(x, router_w, packed, scales, out)
+    _validate(x, router_w, packed, scales, out, dims, int(L))
     if workspace is None:
         workspace = alloc_workspace(dims, topk, x.device)
     st = lib.moe_mxfp4_forward_layers(ctypes.byref(dims.c()), int(L), _ptr(x), _ptr(router_w), _ptr(packed),
@@ -251,7 +262,7 @@ def route(x: torch.Tensor, router_w: torch.Tensor, topk: int, ffn: int, workspac
     T, d = x.shape
     E = router_w.shape[0]
     dims = LayerDims(int(T), int(d), int(ffn), int(E))
-    _validate(x, router_w, None, None, None)
+    _validate(x, router_w, None, None, None, dims)
     if workspace is None:
         workspace = alloc_workspace(dims, topk, x.device)
     dev = x.device
@@ -307,13 +318,18 @@ def quantize(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Opt
              stream=None):
     """MXFP4 quantize/pack of a 2-D fp32 or bf16 device tensor [rows, K] on the GPU
     (moe_mxfp4_quantize): returns (packed uint8 [rows, K/2], scales uint8 [rows, K/32])."""
-    if w.dim() != 2 or w.dtype not in (torch.float32, torch.bfloat16) or not w.is_cuda or not w.is_contiguous():
-        raise ValueError("w must be a contiguous 2-D fp32 or bf16 CUDA tensor")
+    if w.dim() != 2 or w.dtype not in (torch.float32, torch.bfloat16) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D fp32 or bf16 tensor")
     rows, K = w.shape
     if packed is None:
         packed = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
         scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=w.device)
+    for name, t, n in (("packed", packed, rows * (K // 2)), ("scales", scales, rows * (K // 32))):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of {n} elements")
+    if not (w.is_cuda and packed.is_cuda and scales.is_cuda):
+        raise ValueError("w, packed and scales must be device tensors")
     dt = MOE_QDTYPE_F32 if w.dtype == torch.float32 else MOE_QDTYPE_BF16
     _check(lib.moe_mxfp4_quantize(_ptr(w), dt, rows, K, _ptr(packed), _ptr(scales), _stream(stream)), "quantize")
     return packed, scales

@@ -121,3 +121,39 @@ def test_layers_one_launch_choice(moe):
     assert not moe.layers_one_launch(moe.LayerDims(512, 7168, 2048, 256), 8)  # MFMA path
     with pytest.raises(moe.MoeError):
         moe.layers_one_launch(moe.LayerDims(4, 48, 32, 8), 2)
+
+
+def test_binding_checks_buffer_sizes(moe):
+    """The Python binding compares every tensor's element count with the layer
+    sizes (and the quantizer's outputs with its input) before any call, so a
+    short buffer never reaches a kernel; these tensors are on the CPU, so the
+    check must come before the device check."""
+    import torch
+
+    T, d, F, E, k = 4, 64, 64, 8, 2
+    x = torch.zeros((T, d), dtype=torch.bfloat16)
+    wr = torch.zeros((E, d), dtype=torch.float32)
+    p = torch.zeros((E, 3 * d * F // 2), dtype=torch.uint8)
+    s = torch.zeros((E, 3 * d * F // 32), dtype=torch.uint8)
+    dims = moe.LayerDims(T, d, F, E)
+    with pytest.raises(ValueError, match="out has"):
+        moe.forward(x, wr, p, s, k, out=torch.zeros((T - 1, d)), dims=dims)
+    with pytest.raises(ValueError, match="packed has"):
+        moe.forward(x, wr, p[:, :-16].contiguous(), s, k, dims=dims)
+    with pytest.raises(ValueError, match="scales has"):
+        moe.forward(x, wr, p, s[:-1].contiguous(), k, dims=dims)
+    with pytest.raises(ValueError, match="router_w has"):
+        moe.forward(x, wr[:-1].contiguous(), p, s, k, dims=dims)
+    with pytest.raises(ValueError, match="device tensor"):  # right sizes: only the device is wrong
+        moe.forward(x, wr, p, s, k, dims=dims)
+    L = 2
+    with pytest.raises(ValueError, match="packed has"):
+        moe.forward_layers(x, wr.expand(L, E, d).contiguous(), p.expand(L, *p.shape).contiguous()[:, :, :-16]
+                           .contiguous(), s.expand(L, *s.shape).contiguous(), k, dims=dims)
+    w = torch.zeros((3, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="packed must be"):
+        moe.quantize(w, torch.zeros((3, 31), dtype=torch.uint8), torch.zeros((3, 2), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="scales must be"):
+        moe.quantize(w, torch.zeros((3, 32), dtype=torch.uint8), torch.zeros((3, 1), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensors"):
+        moe.quantize(w)
