@@ -1341,8 +1341,10 @@ __device__ __forceinline__ bool stage_h(const Params& P, const Smem& S, uint32_t
   // Staging costs a workgroup barrier and puts the h latency before the
   // first weight loads; it pays where waves would reload h per pass (an expert
   // with more than two tokens) or have few units to spread their own h loads
-  // over (fewer than 8 per wave).
-  const bool worth = __builtin_amdgcn_readfirstlane(many) || q1 - q0 < 8 * kWaves;
+  // over (fewer than 16 per wave: measured on MI355X, a threshold of 16
+  // took the 4-token verify block from 140 to 137 us and left the 8-token one, at
+  // ~26 units per wave, unchanged).
+  const bool worth = __builtin_amdgcn_readfirstlane(many) || q1 - q0 < 16 * kWaves;
   staged = worth && np > 0 && (size_t)np * P.F * 4 <= cap_bytes;
   hb0 = pb;
   if (!staged) return true;
