@@ -87,3 +87,45 @@ def test_decision_points_and_edges(env):
     w = np.array(rows, dtype=np.float32)
     print(f"\n[quant] {w.shape[0]} hand-built rows", flush=True)
     _check(env, w, "decision points")
+
+
+def test_device_quantized_weights_feed_the_layer(env):
+    """Expert weights prepared on the device (fp32 gate, up and down matrices
+    quantized by moe_mxfp4_quantize into the layer's per-expert layout) give
+    the layer the same bytes as the oracle's quantizer, and the layer on them
+    matches the oracle's layer on the oracle's bytes."""
+    torch, moe, oracle, synth = env
+    from helpers import OUT_TOL, check_routing, rel_err
+
+    cfg = synth.get_config("tiny")  # its routing seed keeps the top-k gap clear of rounding
+    T, d, F, E, k = cfg.T, cfg.d, cfg.F, cfg.E, cfg.k
+    x, wr = synth.routing_inputs(cfg)
+    print(f"\n[quant] device-quantized experts T={T} d={d} F={F} E={E} k={k}", flush=True)
+    packs, scs, ref_p, ref_s = [], [], [], []
+    for e in range(E):
+        gu = synth.normals(21, 50, e, 2 * F * d, 0.02).reshape(2 * F, d)   # gate rows, then up rows
+        dn = synth.normals(21, 51, e, d * F, 0.02).reshape(d, F)
+        pg, sg = moe.quantize(torch.from_numpy(gu).cuda())
+        pd, sd = moe.quantize(torch.from_numpy(dn).cuda())
+        packs.append(torch.cat([pg.reshape(-1), pd.reshape(-1)]))
+        scs.append(torch.cat([sg.reshape(-1), sd.reshape(-1)]))
+        Pg, Sg = oracle.quantize(gu.astype(np.float64))
+        Pd, Sd = oracle.quantize(dn.astype(np.float64))
+        ref_p.append(np.concatenate([Pg.ravel(), Pd.ravel()]))
+        ref_s.append(np.concatenate([Sg.ravel(), Sd.ravel()]))
+    pt, st = torch.stack(packs), torch.stack(scs)
+    P, S = np.stack(ref_p), np.stack(ref_s)
+    torch.cuda.synchronize()
+    assert (pt.cpu().numpy() == P).all() and (st.cpu().numpy() == S).all()
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = moe.alloc_workspace(moe.LayerDims(T, d, F, E), k)
+    out = moe.forward(xt, torch.from_numpy(wr).cuda(), pt, st, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert moe.status(ws) == moe.MOE_OK
+    ref = oracle.forward(x, wr, P, S, k, F)
+    assert ref.min_gap > 1e-3
+    it = {n: v.cpu().numpy() for n, v in moe.intermediates(ws, moe.LayerDims(T, d, F, E), k).items()}
+    check_routing(it["topk_idx"], it["topk_w"], it["offsets"], it["sorted_slot"], ref, k)
+    err = rel_err(out.cpu().numpy().astype(np.float64), ref.out)
+    print(f"[quant] layer on device-quantized experts: err {err:.2e}", flush=True)
+    assert err <= OUT_TOL
