@@ -99,6 +99,18 @@ def test_small_shapes_staged(env, shape):
     run_case(env, cfg, staged=True)
 
 
+MAXIMA = [
+    dict(T=4, d=64, F=32, E=1024, k=64),      # E and k at the library's maxima
+    dict(T=2, d=8192, F=4096, E=2, k=2),      # d and ffn at the library's maxima
+]
+
+
+@pytest.mark.parametrize("shape", MAXIMA, ids=lambda s: "T{T}_d{d}_F{F}_E{E}_k{k}".format(**s))
+def test_maximum_sizes(env, shape):
+    """The largest E, top-k, d and ffn the library accepts (include/moe_mxfp4.h)."""
+    run_case(env, env[3].Config("max", **shape))
+
+
 def test_tiny_workload(env):
     cfg = env[3].get_config("tiny")
     run_case(env, cfg)
