@@ -247,8 +247,8 @@ int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
  *                   launch, for sizes on the small-batch path with x of every
  *                   token in LDS (moe_mxfp4_layers_one_launch), else
  *                   MOE_ESHAPE.  Measured on MI355X (8 verify-block layers):
- *                   one launch per operator 265 us per layer, one resident
- *                   launch 278 us: back-to-back launches from one stream leave
+ *                   one launch per operator ~250 us per layer, one resident
+ *                   launch ~268 us: back-to-back launches from one stream leave
  *                   no measurable gap, so the default is the per-operator one.
  * In the one launch, the workgroups meet between layers: each publishes its
  * part of the stream and raises an arrival word; once every arrival word has

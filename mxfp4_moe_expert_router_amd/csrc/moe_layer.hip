@@ -2271,8 +2271,8 @@ __global__ void __launch_bounds__(kWG) k_norm(Params P) {
 // tag, acquires (dropping its CU's and XCD's stale lines) and normalises r
 // into its LDS itself (every workgroup gets the same bits, see norm_rows).
 // The router's first weight loads are already in flight during the wait.
-// Measured on MI355X (8 verify-block layers): one launch 278 us per layer,
-// one launch per operator 265 us: back-to-back launches on one stream leave
+// Measured on MI355X (8 verify-block layers): one launch ~268 us per layer,
+// one launch per operator ~250 us: back-to-back launches on one stream leave
 // no measurable gap between kernels, and this kernel's layer loop costs
 // registers (its hot loops reload some spilled values from scratch).
 
