@@ -72,7 +72,14 @@ constexpr int kMaxK = 64;
 constexpr int kMaxD = 8192;
 constexpr int kMaxF = 4096;
 constexpr int kGUChunks = 4;           // 16-byte chunks per lane of a d-row (d <= 8192)
-constexpr int kGUTok = 4;              // tokens per pass over a decoded gate/up row pair
+// Tokens per pass over a decoded gate/up row pair: 2 with x of every token in
+// LDS (experts of the 1-8 token blocks mostly have one or two tokens; on
+// MI355X 2 instead of 4 took the 8-token verify block from 248.6 to 246.0 us,
+// the 4-token one from 140.5 to 134.9 and decode from 54.7 to 53.4, while the
+// shared-routing 8-token block, with up to 7 tokens per expert, went from
+// 185.4 to 188.0), 4 with x of the workgroup's own pairs (16-32 tokens).
+template <bool XP>
+constexpr int kGUTok = XP ? 4 : 2;
 constexpr int kDnRows = 8;             // W_down rows per down step (at most; reduce8 width)
 constexpr int kMaxGrid = 2048;
 constexpr int kMaxLayers = 4096;        // layers of one stack call
@@ -955,11 +962,11 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
   const int xb0 = XP ? uni(S.misc[kMiscXBase]) : 0, xn = XP ? uni(S.misc[kMiscXRows]) : 0;
   const auto group = [&](int tb, auto global_x) {
     constexpr bool GX = decltype(global_x)::value;
-    const int nb = min(kGUTok, ne - tb);
-    float g[kGUTok], u[kGUTok];
-    int xrow[kGUTok];
+    const int nb = min(kGUTok<XP>, ne - tb);
+    float g[kGUTok<XP>], u[kGUTok<XP>];
+    int xrow[kGUTok<XP>];
 #pragma unroll
-    for (int t = 0; t < kGUTok; ++t) {
+    for (int t = 0; t < kGUTok<XP>; ++t) {
       g[t] = u[t] = 0.f;
       const int pr = p0 + tb + t;
       xrow[t] = t < nb ? (GX || !XP ? uni(S.slot[pr]) / P.k : pr - xb0) : 0;
@@ -972,7 +979,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
         decode32_bf16(R.u[m], e8m0_to_f32(R.su[m]), du);
         const int cc = min(lane + kWave * m, NCH - 1);
 #pragma unroll
-        for (int t = 0; t < kGUTok; ++t) {
+        for (int t = 0; t < kGUTok<XP>; ++t) {
           if (t < nb) {
             u32x4_t xq[4];
             if (GX) {
@@ -991,7 +998,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
       }
     }
 #pragma unroll
-    for (int t = 0; t < kGUTok; ++t) {
+    for (int t = 0; t < kGUTok<XP>; ++t) {
       if (t < nb) {
         const float gs = wave_sum(g[t]), us = wave_sum(u[t]);
         if (lane == 0)
@@ -1000,7 +1007,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
     }
   };
   const auto run = [&](int tb) {
-    const int nb = min(kGUTok, ne - tb);
+    const int nb = min(kGUTok<XP>, ne - tb);
     if (!XP || (p0 + tb >= xb0 && p0 + tb + nb <= xb0 + xn))  // uniform
       group(tb, std::false_type{});
     else
@@ -1010,7 +1017,7 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
   // body reads the row pair's registers makes the compiler wait for every
   // load in flight (vmcnt(0)) at its entry, including the next row pair's.
   run(0);
-  for (int tb = kGUTok; tb < ne; tb += kGUTok) run(tb);
+  for (int tb = kGUTok<XP>; tb < ne; tb += kGUTok<XP>) run(tb);
 }
 
 // xmode 1: x rows of the pairs of the experts the workgroup's gate/up range
