@@ -635,10 +635,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 
 // Work model of the expert steps, per row of an expert with n tokens (from
 // per-workgroup timings on MI355X): a gate/up row pair costs 16 + 5 per extra
-// token (the weights are read and decoded once, the dot products repeat);
+// token (the weights are read once, the dot products repeat) + 4 per extra
+// group of g tokens (g = kGUTok of the variant: the row pair is decoded again
+// for each group; the term took the shared-routing 8-token block, with up to
+// 7 tokens per expert, from 188.4 to 184.7 us and left the others unchanged);
 // a W_down row costs 10 per pass over the row plus 4 for the second token of
 // a two-token pass (F <= 2048 takes tokens two at a time).
-__device__ __forceinline__ int gu_cost(int n) { return 16 + 5 * (n - 1); }
+__device__ __forceinline__ int gu_cost(int n, int g) { return 16 + 5 * (n - 1) + 4 * ((n + g - 1) / g - 1); }
 __device__ __forceinline__ int dn_cost(int n, int F) { return F <= 2048 ? 14 * (n / 2) + 10 * (n % 2) : 10 * n; }
 
 // Work model of the MFMA path, per workgroup unit of an expert with n tokens:
@@ -737,7 +740,7 @@ __device__ __forceinline__ void build_perm_wave(const Params& P, const Smem& S, 
     }
     if (lane == 0) S.misc[0] = na;
     const int n = lane < na ? S.cgu[lane] : 0;
-    const int g = lane < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n)) : 0;
+    const int g = lane < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
     const int dc = lane < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
     const int gi = wave_inclusive_scan(g), di = wave_inclusive_scan(dc);
     if (lane < na) {
@@ -836,7 +839,7 @@ __device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool 
     for (int i = 0; i < 2; ++i) {
       const int a = e0 + i;
       const int n = a < na ? S.off[S.act[a] + 1] - S.off[S.act[a]] : 0;
-      g2[i] = a < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n)) : 0;
+      g2[i] = a < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
       d2[i] = a < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
       gs += g2[i];
       ds += d2[i];
