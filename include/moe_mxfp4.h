@@ -288,6 +288,28 @@ enum { MOE_QDTYPE_F32 = 0, MOE_QDTYPE_BF16 = 1 };
 int moe_mxfp4_quantize(const void* w, int32_t dtype, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
                        void* stream);
 
+/* ---- MXFP4 codec on the host ([P3-FP4] "FP4：只量化 MoE expert，其餘維持原精度":
+ * each small block of weights is stored as 4-bit values plus one shared
+ * scale; [MX] E2M1 elements, 32-element blocks, E8M0 scales 2^(s-127)).  Host
+ * memory only; nothing is enqueued and no GPU is needed.
+ *
+ * moe_mxfp4_quantize_host: rows x K fp32 values (row-major, host) -> packed
+ * [rows][K/2] codes (element c of a row in byte c/2, low nibble for even c)
+ * and scales [rows][K/32] E8M0 bytes, by the rule of moe_mxfp4_quantize
+ * (X = floor(log2 max|v|) - 2 clamped to [-127, 127], -127 for an all-zero
+ * block; nearest E2M1 magnitude of |v| / 2^X, ties to the even mantissa bit,
+ * saturating at 6; sign bit when v < 0, so -0 gives code 0).
+ * moe_mxfp4_dequantize_host: the reverse, value = E2M1(code) * 2^(s-127)
+ * rounded to fp32: exact whenever the product is an fp32 value (every code at
+ * s <= 252), +-inf where it exceeds the fp32 range (large codes at s = 253,
+ * 254), NaN for s = 255.
+ * Errors: MOE_EINVAL (null pointer with rows, K > 0; negative size; a
+ * non-finite input value to quantize, checked before anything is written),
+ * MOE_ESHAPE (K not a multiple of 32).  rows = 0 or K = 0 does nothing.  The
+ * caller owns every buffer. */
+int moe_mxfp4_quantize_host(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales);
+int moe_mxfp4_dequantize_host(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K, float* w);
+
 #ifdef __cplusplus
 }
 #endif

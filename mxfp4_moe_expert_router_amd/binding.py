@@ -84,6 +84,10 @@ def _load():
     lib.moe_mxfp4_layers_one_launch.restype = ctypes.c_int
     lib.moe_mxfp4_layers_one_launch.argtypes = [P(Dims), i32]
     lib.moe_mxfp4_quantize.argtypes = [vp, i32, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+    lib.moe_mxfp4_quantize_host.restype = ctypes.c_int
+    lib.moe_mxfp4_quantize_host.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]
+    lib.moe_mxfp4_dequantize_host.restype = ctypes.c_int
+    lib.moe_mxfp4_dequantize_host.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     return lib
 
 
@@ -333,3 +337,35 @@ def quantize(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Opt
     dt = MOE_QDTYPE_F32 if w.dtype == torch.float32 else MOE_QDTYPE_BF16
     _check(lib.moe_mxfp4_quantize(_ptr(w), dt, rows, K, _ptr(packed), _ptr(scales), _stream(stream)), "quantize")
     return packed, scales
+
+
+def quantize_host(w):
+    """MXFP4 quantize/pack of a 2-D fp32 host array [rows, K] in the library's
+    host code (moe_mxfp4_quantize_host): returns (packed uint8 [rows, K/2],
+    scales uint8 [rows, K/32]) as numpy arrays."""
+    import numpy as np
+
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    rows, K = w.shape
+    packed = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // 32), dtype=np.uint8)
+    _check(lib.moe_mxfp4_quantize_host(w.ctypes.data, rows, K, packed.ctypes.data, scales.ctypes.data),
+           "quantize_host")
+    return packed, scales
+
+
+def dequantize_host(packed, scales, rows: int, K: int):
+    """MXFP4 codes and scales (host arrays) -> fp32 [rows, K]
+    (moe_mxfp4_dequantize_host)."""
+    import numpy as np
+
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if packed.size != rows * (K // 2) or scales.size != rows * (K // 32):
+        raise ValueError("packed / scales sizes do not match rows and K")
+    w = np.empty((rows, K), dtype=np.float32)
+    _check(lib.moe_mxfp4_dequantize_host(packed.ctypes.data, scales.ctypes.data, rows, K, w.ctypes.data),
+           "dequantize_host")
+    return w

@@ -22,7 +22,9 @@
 // depend on how the hardware treats subnormal operands.  HBM-bound: 4.5 bytes
 // per element (fp32 in) or 2.5 (bf16 in).
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "moe_mxfp4.h"
 
@@ -222,5 +224,114 @@ extern "C" int moe_mxfp4_quantize(const void* w, int32_t dtype, int64_t rows, in
     hipLaunchKernelGGL(moe_q::k_quantize<false>, dim3((unsigned)grid), dim3(moe_q::kThreads), 0, s, w, nblocks,
                        packed, scales);
   if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ host codec ---
+// The same format on the host ([P3-FP4] 4-bit values plus one shared scale
+// per small block; [MX] E2M1 elements, 32-element blocks, E8M0 scales), for
+// callers that prepare or inspect expert weights in host memory.  Plain C++:
+// the shared exponent comes from the fp32 bit pattern of the block maximum,
+// the codes from a table of the rounding rule's decision points (the
+// midpoints of neighbouring E2M1 magnitudes, which are exact in double).
+
+namespace moe_q {
+
+// floor(log2 a) for the bit pattern a (sign cleared) of a nonzero finite fp32.
+static int host_ilog2(uint32_t a) {
+  const int ex = (int)(a >> 23);
+  if (ex > 0) return ex - 127;
+  return (31 - __builtin_clz(a)) - 149;  // subnormal
+}
+
+static uint32_t host_bits(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  return u;
+}
+
+// E2M1 magnitude code (0..7) of q = |v| / 2^X >= 0: the nearest of 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6; at a midpoint the code with an even mantissa bit (even
+// code), which is the lower neighbour at 0.25, 1.25, 2.5, 5 and the upper one
+// at 0.75, 1.75, 3.5; above 6 the largest magnitude.
+static uint32_t host_e2m1_code(double q) {
+  if (q <= 0.25) return 0;
+  if (q < 0.75) return 1;
+  if (q <= 1.25) return 2;
+  if (q < 1.75) return 3;
+  if (q <= 2.5) return 4;
+  if (q < 3.5) return 5;
+  if (q <= 5.0) return 6;
+  return 7;
+}
+
+// E2M1 code -> value: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
+// exponent field 0 holds 0 and 0.5.
+static float host_e2m1_value(uint32_t code) {
+  static const float kMag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float m = kMag[code & 7u];
+  return (code & 8u) ? -m : m;
+}
+
+}  // namespace moe_q
+
+extern "C" int moe_mxfp4_quantize_host(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales) {
+  using namespace moe_q;
+  if (rows < 0 || K < 0) return MOE_EINVAL;
+  if (K % 32) return MOE_ESHAPE;
+  if (rows == 0 || K == 0) return MOE_OK;
+  if (!w || !packed || !scales) return MOE_EINVAL;
+  const int64_t n = rows * K;
+  for (int64_t i = 0; i < n; ++i)
+    if ((host_bits(w[i]) & 0x7F800000u) == 0x7F800000u) return MOE_EINVAL;  // inf or NaN
+  const int64_t nb = K / 32;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* v = w + r * K + b * 32;
+      uint32_t amax = 0;
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t a = host_bits(v[i]) & 0x7FFFFFFFu;
+        if (a > amax) amax = a;  // finite fp32 magnitudes order like their bit patterns
+      }
+      int X = amax == 0 ? -127 : host_ilog2(amax) - 2;
+      if (X < -127) X = -127;
+      if (X > 127) X = 127;
+      scales[r * nb + b] = (uint8_t)(X + 127);
+      uint8_t* out = packed + r * (K / 2) + b * 16;
+      for (int i = 0; i < 32; i += 2) {
+        uint32_t c[2];
+        for (int h = 0; h < 2; ++h) {
+          const float x = v[i + h];
+          const double q = ldexp(fabs((double)x), -X);  // exact: a power-of-two scaling of an fp32 value
+          c[h] = host_e2m1_code(q) | ((host_bits(x) >> 31) && x != 0.0f ? 8u : 0u);
+        }
+        out[i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+      }
+    }
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_mxfp4_dequantize_host(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
+                                         float* w) {
+  using namespace moe_q;
+  if (rows < 0 || K < 0) return MOE_EINVAL;
+  if (K % 32) return MOE_ESHAPE;
+  if (rows == 0 || K == 0) return MOE_OK;
+  if (!packed || !scales || !w) return MOE_EINVAL;
+  const int64_t nb = K / 32;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint32_t s = scales[r * nb + b];
+      // 2^(s-127) in double (exact for every byte), NaN for 255
+      const double sc = s == 255u ? (double)NAN : ldexp(1.0, (int)s - 127);
+      const uint8_t* in = packed + r * (K / 2) + b * 16;
+      float* o = w + r * K + b * 32;
+      for (int i = 0; i < 16; ++i) {
+        o[2 * i] = (float)((double)host_e2m1_value(in[i] & 0xFu) * sc);
+        o[2 * i + 1] = (float)((double)host_e2m1_value(in[i] >> 4) * sc);
+      }
+    }
+  }
   return MOE_OK;
 }
