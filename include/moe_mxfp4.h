@@ -47,7 +47,14 @@
  *  h = silu(W_gate x_t) * (W_up x_t), y = W_down h (dequantized weights, fp32
  *  accumulation, h kept in fp32);
  *  out[t] = sum_j gate[t][j] * y(expert_j, t), summed in top-k order.
- *  Supported scale bytes on the GPU: 1..254 (0 decodes as 0, 255 as +inf).
+ *  Scale bytes: every byte s in 0..254 decodes as 2^(s-127), byte 0 included
+ *  (2^-127, with subnormal element values kept, as measured on MI355X and
+ *  checked against the fp64 oracle by the GPU tests); an element whose value
+ *  exceeds the fp32 range (a large code at s = 253 or 254) decodes as +-inf.
+ *  Byte 255 (NaN in the format) is not supported.
+ *  h: kept in fp32 on the small-batch path; on the MFMA path (more than 48
+ *  tokens whose x does not fit in LDS) the down projection takes h as the sum
+ *  of two bf16 values (hi, lo), i.e. to about 16 significant bits.
  *
  * Ownership and concurrency: the caller allocates and frees every buffer.  The
  * library never allocates device memory, never synchronizes (except
@@ -130,9 +137,13 @@ int moe_mxfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stre
  *   workspace       device, 256-byte aligned, >= moe_mxfp4_workspace_bytes(),
  *                   zero-filled before its first use
  *   stream          hipStream_t
- * Returns MOE_OK once enqueued.  Every device-side wait has a watchdog (2 s);
- * a wait that does not finish makes the kernel exit early and sets the status
- * word that moe_mxfp4_status() returns as MOE_ETIMEOUT. */
+ * Returns MOE_OK once enqueued.  Every device-side wait on another
+ * workgroup's results has a watchdog (2 s); a wait that does not finish makes
+ * the kernel exit early and sets the status word that moe_mxfp4_status()
+ * returns as MOE_ETIMEOUT.  The out elements such a call could not complete
+ * are then NaN (each wave whose wait was abandoned writes NaN into all of the
+ * elements it combines), so out never keeps an earlier call's values; the
+ * others hold this call's results. */
 int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
                       const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -172,6 +183,11 @@ typedef struct {
  * at once as long as no other kernel holds CUs, and if one does, the layer's
  * waits end with MOE_ETIMEOUT instead of hanging. */
 #define MOE_OPT_COOPERATIVE 0x4u
+
+/* Test knob: the down step waits for h words tagged for a call that never
+ * happens, so every down wait reaches its watchdog; the call ends with
+ * MOE_ETIMEOUT and every element of out NaN. */
+#define MOE_OPT_WITHHOLD_H 0x8u
 
 /* moe_mxfp4_forward with options (opts may be NULL). */
 int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
@@ -236,8 +252,8 @@ int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
  *   scales          [L] x the layer's E experts, layer l at byte
  *                   l*E*moe_mxfp4_expert_scale_bytes(d, F) (device)
  *   out             fp32 [T][d] = r_L (device, 16-byte aligned, fully
- *                   overwritten; it holds r_l while the stack runs, so it
- *                   must not overlap any input)
+ *                   overwritten; it holds intermediate r_l while the stack
+ *                   runs, so it must not overlap any input)
  *   workspace       as for moe_mxfp4_forward (same size).  After the call its
  *                   inspection copies describe the last layer, and x_last
  *                   (moe_mxfp4_ws_layout) holds that layer's input.
@@ -255,10 +271,15 @@ int moe_mxfp4_persistent_grid(const moe_mxfp4_dims* dims, int32_t topk);
  * moved on, each workgroup normalises the stream into its LDS and the next
  * layer's router starts (its first weight loads are issued before the wait).  Errors as moe_mxfp4_forward, and
  * MOE_EINVAL for L out of range or unknown / conflicting flags.  A device
- * wait that times out stops the stack (MOE_ETIMEOUT from moe_mxfp4_status;
- * out is then undefined). */
+ * wait that times out stops the stack (MOE_ETIMEOUT from moe_mxfp4_status);
+ * the elements of out it could not complete are then NaN, as for
+ * moe_mxfp4_forward (in the one-launch mode every element a stopped
+ * workgroup combines). */
 #define MOE_LAYERS_PER_LAUNCH 0x1
 #define MOE_LAYERS_ONE_LAUNCH 0x2
+/* Either mode, launched cooperatively (see MOE_OPT_COOPERATIVE): the runtime
+ * then guarantees that each launch's workgroups are resident at once. */
+#define MOE_LAYERS_COOPERATIVE 0x4
 int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const void* x, const float* router_w,
                              const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
                              void* workspace, size_t workspace_bytes, int32_t flags, void* stream);

@@ -21,9 +21,11 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ETIMEOUT, MOE_E
 MOE_OPT_WITHHOLD_ARRIVAL = 0x1
 MOE_OPT_TRACE = 0x2
 MOE_OPT_COOPERATIVE = 0x4
+MOE_OPT_WITHHOLD_H = 0x8
 MOE_QDTYPE_F32, MOE_QDTYPE_BF16 = 0, 1
 MOE_LAYERS_PER_LAUNCH = 0x1
 MOE_LAYERS_ONE_LAUNCH = 0x2
+MOE_LAYERS_COOPERATIVE = 0x4
 
 
 class MoeError(RuntimeError):

@@ -126,6 +126,7 @@ struct Params {
   uint64_t* trace;    // [grid][kTraceSlots] wall-clock stamps, or null
   uint64_t spin_ticks;
   uint32_t withhold;  // test knob: top-k waits for a tag the router never writes
+  uint32_t withhold_h;  // test knob: the down step waits for a tag gate/up never writes
   int mfma;           // 1: x does not fit in LDS, expert steps on MFMA
   int xmode;          // small-batch path: 0 x of every token in LDS, 1 x of the workgroup's pairs (see stage_pairs)
   int xrows;          // small-batch path: rows of x the LDS holds
@@ -135,6 +136,10 @@ struct Params {
   // adds the layer's output to r, which out holds.
   int stack_layers;   // L of the stack; 0: a lone layer (out = layer(x))
   int layer0;         // stack index of the launch's first layer
+  const float* rin;   // stack: r_l of the layer (layer 0 reads x0 instead)
+  float* rout;        // stack: where the layer writes r_{l+1}
+  float* rbuf;        // stack: fp32 [T][d] workspace buffer; the one-launch stack
+                      // alternates r between it and out (see k_stack)
   int nlayers;        // layers this launch runs (k_stack), 1 otherwise
   const uint16_t* x0; // the stack's input, bf16 [T][d] (r_0)
   uint16_t* xb;       // bf16 [T][d]: a layer's normalised input (the last one's after a call)
@@ -1147,6 +1152,7 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
   const int lane = threadIdx.x & (kWave - 1);
   const int NCH = P.F / 32;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq + (size_t)p * P.F, (uint32_t)P.F * 8u);
+  const uint32_t want = tag + P.withhold_h;
   const uint64_t t0 = wall_clock64();
   int round = 0;
   // The first attempt reads the whole h at once and through the L2 (it is
@@ -1163,7 +1169,7 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const u32x4_t w = round == 0 ? ld_cached16(rs, base + v * 16u) : ld_coherent16(rs, base + v * 16u);
-        ok &= (w.y == tag) && (w.w == tag);
+        ok &= (w.y == want) && (w.w == want);
         h[m][2 * v] = c < NCH ? u2f(w.x) : 0.f;
         h[m][2 * v + 1] = c < NCH ? u2f(w.z) : 0.f;
       }
@@ -1175,7 +1181,7 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
     bool go = true;
     if (round > 0) {  // uniform
       const u32x4_t q = ld_coherent16(rs, probe);
-      go = __all((q.y == tag) && (q.w == tag));
+      go = __all((q.y == want) && (q.w == want));
     }
     if (go && read_all()) return true;
     if (!keep_waiting(P, tag, t0, kSiteH, p, round, 3)) return false;
@@ -1371,7 +1377,7 @@ __device__ __forceinline__ bool stage_h(const Params& P, const Smem& S, uint32_t
     for (int i = threadIdx.x; i < n16; i += kWG) {
       // first read through the L2 (dropped of earlier calls' lines, see k_layer)
       const u32x4_t w = round == 0 ? ld_cached16(rs, (uint32_t)i * 16u) : ld_coherent16(rs, (uint32_t)i * 16u);
-      if (w.y == tag && w.w == tag) {
+      if (w.y == tag + P.withhold_h && w.w == tag + P.withhold_h) {
         hl[2 * i] = u2f(w.x);
         hl[2 * i + 1] = u2f(w.z);
       } else {
@@ -1878,12 +1884,13 @@ __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __a
 }
 
 // Checks the tags of a staged h tile (re-reading it until they are current;
-// after a watchdog abort it gives up and the data is not used), then writes it
+// after a watchdog abort it gives up and sets *bad, an LDS flag after which
+// the workgroup stores no more results), then writes it
 // as bf16 hi and lo tiles, layout [block][pair][272 bytes] each.  Values past
 // the pass or past F are zero.
 __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
                                                uint32_t tag, u32x4_t (&v)[kHPieces], char* hi_tile,
-                                               char* lo_tile) {
+                                               char* lo_tile, int* bad) {
   const int np = min(kDnPass, c.ne - c.pass);
   auto used = [&](int m) {
     const int pc = (int)threadIdx.x + kWG * m;
@@ -1892,14 +1899,19 @@ __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __
   auto current = [&]() {
     bool ok = true;
 #pragma unroll
-    for (int m = 0; m < kHPieces; ++m) ok &= !used(m) || (v[m].y == tag && v[m].w == tag);
+    for (int m = 0; m < kHPieces; ++m) ok &= !used(m) || (v[m].y == tag + P.withhold_h && v[m].w == tag + P.withhold_h);
     return ok;
   };
   if (!__all(current())) {
     const uint64_t t0 = wall_clock64();
     int round = 0;
     for (;;) {
-      if (!keep_waiting(P, tag, t0, kSiteH, c.p0 + c.pass, round, 3)) break;
+      if (!keep_waiting(P, tag, t0, kSiteH, c.p0 + c.pass, round, 3)) {
+        // the tile is written anyway (every wave keeps to the workgroup's
+        // barriers), but no result computed from it is stored
+        *bad = 1;
+        break;
+      }
       dn_mfma_hload<true>(P, c, rs, v);
       if (__all(current())) break;
     }
@@ -2001,8 +2013,11 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
 __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
                                             int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
                                             const DnA& Ac, DnA& An, char* cur, char* nxt,
-                                            f32x4_t (&acc)[kDnTiles][2]) {
+                                            f32x4_t (&acc)[kDnTiles][2], int* bad) {
   constexpr int kHalf = kDnK * kDnPass * kTileRow;  // hi tile; lo tile follows
+  // read after the barrier that ended the previous step: set if any tile up to
+  // the current one failed its wait (the flag never clears within a call)
+  const bool ok = *bad == 0;
   u32x4_t hr[kHPieces];
   dn_mfma_hload<false>(P, nc, rs, hr);  // first: waiting for it below must not wait for An
   dn_mfma_load(P, nc, R, An);
@@ -2010,20 +2025,24 @@ __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint
     dn_mfma_step<2>(Ac, cur, cur + kHalf, acc);
   else
     dn_mfma_step<1>(Ac, cur, cur + kHalf, acc);
-  if (cc.j == nst - 1) dn_mfma_store(P, S, cc, R, tag, acc);
-  if (q + 1 < npos) dn_mfma_hstore(P, nc, rs, tag, hr, nxt, nxt + kHalf);
+  if (cc.j == nst - 1 && ok) dn_mfma_store(P, S, cc, R, tag, acc);
+  if (q + 1 < npos) dn_mfma_hstore(P, nc, rs, tag, hr, nxt, nxt + kHalf, bad);
   seg_next(S, U1, R, nst, kDnPass, cc);
   seg_next(S, U1, R, nst, kDnPass, nc);
   lds_barrier();
 }
 
-// Down projection for the workgroup's units [U0, U1).  All threads.
-__device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+// Down projection for the workgroup's units [U0, U1).  All threads.  False
+// if an h wait was abandoned (then some of the units' results are not stored).
+__device__ __forceinline__ bool down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  __shared__ int s_bad;
   const int R = (P.d + kDnUnitRows - 1) / kDnUnitRows;
   const int nst = (P.F + kDnK * kKB - 1) / (kDnK * kKB);
   const int U0 = uni(S.misc[6]), U1 = uni(S.misc[4]);
   const int npos = seg_count(S, U0, U1, R, nst, kDnPass);
-  if (npos == 0) return;
+  if (npos == 0) return true;
+  if (threadIdx.x == 0) s_bad = 0;
+  lds_barrier();  // before any wave can set it
   constexpr int kHalf = kDnK * kDnPass * kTileRow;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq, (uint32_t)((size_t)P.T * P.k * P.F * 8));
   char* t0 = reinterpret_cast<char*>(S.xs);
@@ -2039,25 +2058,27 @@ __device__ __forceinline__ void down_mfma(const Params& P, const Smem& S, uint32
     u32x4_t hr[kHPieces];
     dn_mfma_hload<false>(P, nc, rs, hr);
     dn_mfma_load(P, nc, R, A0);
-    dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf);
+    dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf, &s_bad);
     seg_next(S, U1, R, nst, kDnPass, nc);
     lds_barrier();
   }
   for (int q = 0; q < npos; q += 2) {
-    dn_mfma_one(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc);
+    dn_mfma_one(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc, &s_bad);
     if (q + 1 >= npos) break;
-    dn_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc);
+    dn_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc, &s_bad);
   }
+  return s_bad == 0;  // after the last step's barrier: the same in every wave
 }
 
 // ---------------------------------------------------------- combine ---------
 // out[t][c] = sum over j < k of the tagged gated rows y[t*k + j][c], in slot
 // order.  Unit = (token, 64 columns), one wave.
 // In a stack (P.stack_layers > 0) the sum goes onto the residual stream:
-// r = (layer 0 ? x0 : out) + sum, written to out with agent-scope
+// r_{l+1} = (layer 0 ? x0 : rin) + sum, written to rout with agent-scope
 // (write-through) stores, which the next layer's workgroups read after the
-// arrival wait without a write-back of the L2.  Each element of out is read
-// and written by the same wave in every layer.
+// arrival wait without a write-back of the L2.  Each element of the stream is
+// read and written by the same wave in every layer.  Returns false if a wait
+// was abandoned (the wave's remaining units are then not written).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite f
@@ -2091,10 +2112,11 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
               a0 = bf16lo(xv) + a0;
               a1 = bf16hi(xv) + a1;
             } else {
-              const float2 r = *o;
+              const float2 r = *reinterpret_cast<const float2*>(P.rin + (size_t)t * P.d + c);
               a0 = r.x + a0;
               a1 = r.y + a1;
             }
+            o = reinterpret_cast<float2*>(P.rout + (size_t)t * P.d + c);
             const uint64_t bits = (uint64_t)__builtin_bit_cast(uint32_t, a0) |
                                   ((uint64_t)__builtin_bit_cast(uint32_t, a1) << 32);
             __hip_atomic_store(reinterpret_cast<uint64_t*>(o), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2108,6 +2130,23 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
     }
   }
   return true;
+}
+
+// A wave whose waits were abandoned (a watchdog fired: MOE_ETIMEOUT) writes
+// NaN into every out element of the combine units it owns (the units of
+// combine_step), so that out never keeps an earlier call's plausible values.
+// Units whose combine completed hold this call's correct sums: every tagged
+// word a combine accepts was computed from complete inputs, because a step
+// whose wait was abandoned stores no tagged results.
+__device__ __forceinline__ void poison_out(const Params& P, float* dst, int gw, int NW) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kCols = 2 * kWave;
+  const int nd = (P.d + kCols - 1) / kCols;
+  const float nan = __builtin_nanf("");
+  for (int u = gw; u < P.T * nd; u += NW) {
+    const int t = u / nd, c = (u % nd) * kCols + 2 * lane;
+    if (c < P.d) *reinterpret_cast<float2*>(dst + (size_t)t * P.d + c) = make_float2(nan, nan);
+  }
 }
 
 // ---------------------------------------------------------- kernels ---------
@@ -2167,11 +2206,14 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
     } else {
       gate_up_mfma(P, S, tag, wg, G);
       stamp(P, wg, 4);
-      down_mfma(P, S, tag, wg, G);
+      dn = down_mfma(P, S, tag, wg, G);
     }
     stamp(P, wg, 5);
-    if (dn) combine_step(P, tag, gw, NW, P.layer0);
+    if (dn) dn = combine_step(P, tag, gw, NW, P.layer0);
     stamp(P, wg, 6);
+    if (!dn) poison_out(P, P.stack_layers > 0 ? P.rout : P.out, gw, NW);
+  } else {
+    poison_out(P, P.stack_layers > 0 ? P.rout : P.out, gw, NW);
   }
   __syncthreads();
   if (wg == 0) end_call(P, tag, G);
@@ -2273,7 +2315,8 @@ __global__ void __launch_bounds__(kWG) k_norm(Params P) {
 // pipeline stays on the GPU, no return to the host between operators;
 // [P5-TRT]: MoE gate then expert compute, per layer).  Layer l runs under tag
 // t0 + l.  Between layers every workgroup publishes its part of the stream r
-// (the combine's stores, agent-scope atomics that write through the L2; each
+// (the combine's stores into out or rbuf, alternating by layer, agent-scope
+// atomics that write through the L2; each
 // wave waits for them to complete, so no L2 write-back is needed: one per wave
 // cost ~45 us per layer), then its arrival word (hdr[kStarted + wg]) takes
 // the next layer's tag.  The next layer's router needs the input of every
@@ -2330,6 +2373,7 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
   int l = 0;
   uint32_t tag = t0;
   int sl = P0.layer0;
+  bool failed = false;
   // The layer loop is entered at its top, and (never: the host passes
   // nlayers >= 1) at its second half: a cycle with two entries is not a
   // natural loop, so the optimizer hoists none of the body's lane-invariant
@@ -2342,6 +2386,16 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
     P.wr = P0.wr + (size_t)l * P0.wr_stride;
     P.packed = P0.packed + (size_t)l * P0.pk_stride;
     P.scales = P0.scales + (size_t)l * P0.sc_stride;
+    // The stream alternates between two buffers: layer sl writes r_{sl+1} to
+    // out if L - 1 - sl is even, else to rbuf (so the last layer's lands in
+    // out), and reads r_sl where layer sl - 1 wrote it.  A buffer is written
+    // again only two layers after it was read, i.e. after every workgroup's
+    // arrival at the layer in between, so a workgroup still normalising r_sl
+    // never sees it overwritten.  (With one buffer, a workgroup whose results
+    // nothing waited for could still be reading r_sl while others already
+    // wrote r_{sl+1} over it.)
+    P.rout = ((P0.stack_layers - 1 - sl) & 1) ? P0.rbuf : P0.out;
+    P.rin = ((P0.stack_layers - sl) & 1) ? P0.rbuf : P0.out;
     if (threadIdx.x == 0) s_ok = s_go = 1;
     __syncthreads();
     router_step<true>(P, S, tag, wg, G, [&] {
@@ -2355,11 +2409,14 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
       }
       // workgroup 0 also leaves the last layer's input in xb, for inspection
       if (s_go)
-        norm_rows(P, sl == 0 ? nullptr : P.out, sl == 0 ? P.x0 : nullptr, 0, P.T, S.xs,
+        norm_rows(P, sl == 0 ? nullptr : P.rin, sl == 0 ? P.x0 : nullptr, 0, P.T, S.xs,
                   (wg == 0 && l == P0.nlayers - 1) ? P0.xb : nullptr);
       __syncthreads();
     });
-    if (!s_go) break;  // uniform
+    if (!s_go) {  // uniform
+      failed = true;
+      break;
+    }
   second_half:
     {
       bool ok = topk_publish(P, tag, gw, NW);
@@ -2368,7 +2425,10 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
       __syncthreads();
       if (!ok) s_ok = 0;
       __syncthreads();
-      if (!s_ok) break;  // uniform
+      if (!s_ok) {  // uniform
+        failed = true;
+        break;
+      }
       build_perm(P, S, wg == 0);
       set_ranges(P, S, wg, G);
       if (wg < 8 && threadIdx.x >= kWG - kWave) invalidate_l2();
@@ -2380,11 +2440,17 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
       __builtin_amdgcn_s_waitcnt(0);
       if (threadIdx.x == 0 && stack_aborted(P0, t0)) s_ok = 0;
       __syncthreads();
-      if (!s_ok) break;  // uniform
+      if (!s_ok) {  // uniform
+        failed = true;
+        break;
+      }
     }
     if (++l >= P0.nlayers) break;
     if (threadIdx.x == 0) st_relaxed(&P0.hdr[kStarted + wg], tag + 1u);
   }
+  // a stack stopped by an abandoned wait leaves NaN in the out elements of
+  // the workgroup's combine units (see poison_out)
+  if (failed) poison_out(P0, P0.out, gw, NW);
   // a workgroup that stopped early still closes its arrival word, so that
   // the end of the launch does not wait for it
   __syncthreads();
@@ -2468,7 +2534,8 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
   const uint32_t tag = start_call(P, blockIdx.x, false);
-  combine_step(P, tag, blockIdx.x * kWaves + uni(threadIdx.x / kWave), gridDim.x * kWaves, P.layer0);
+  const int gw = blockIdx.x * kWaves + uni(threadIdx.x / kWave), NW = gridDim.x * kWaves;
+  if (!combine_step(P, tag, gw, NW, P.layer0)) poison_out(P, P.stack_layers > 0 ? P.rout : P.out, gw, NW);
 }
 __global__ void k_st_bump(Params P) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
@@ -2499,7 +2566,7 @@ static int check_dims(const moe_mxfp4_dims* dm, int32_t topk) {
 
 struct Layout {
   size_t hdr, lgp, tk, hq, yq, logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, trace, xb,
-      total;
+      rb, total;
 };
 
 static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
@@ -2521,6 +2588,7 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
   L.n_active = o; o = align_up(o + 4);
   L.trace = o; o = align_up(o + (size_t)kMaxGrid * kTraceSlots * 8);
   L.xb = o; o = align_up(o + T * (size_t)dm->d * 2);
+  L.rb = o; o = align_up(o + T * (size_t)dm->d * 4);
   L.total = o;
   return L;
 }
@@ -2628,6 +2696,7 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   const uint64_t us = spin_us ? spin_us : 2000000u;
   P.spin_ticks = us * di.ticks_per_us;
   P.withhold = 0;
+  P.withhold_h = 0;
   P.mfma = 0;
   P.xmode = 0;
   P.xrows = 0;
@@ -2637,6 +2706,9 @@ static Params make_params(const moe_mxfp4_dims* dm, int32_t k, const void* x, co
   P.nlayers = 1;
   P.xb = reinterpret_cast<uint16_t*>(b + L.xb);
   P.x0 = static_cast<const uint16_t*>(x);
+  P.rin = out;
+  P.rout = out;
+  P.rbuf = reinterpret_cast<float*>(b + L.rb);
   P.wr_stride = P.pk_stride = P.sc_stride = 0;
   return P;
 }
@@ -2817,7 +2889,8 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
                          void* workspace, size_t workspace_bytes, const moe_mxfp4_options* opts, void* stream) {
   int st = check_dims(dims, topk);
   if (st != MOE_OK) return st;
-  if (opts && (opts->flags & ~(MOE_OPT_WITHHOLD_ARRIVAL | MOE_OPT_TRACE | MOE_OPT_COOPERATIVE))) return MOE_EINVAL;
+  if (opts && (opts->flags & ~(MOE_OPT_WITHHOLD_ARRIVAL | MOE_OPT_TRACE | MOE_OPT_COOPERATIVE | MOE_OPT_WITHHOLD_H)))
+    return MOE_EINVAL;
   if (opts && opts->grid < 0) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;  // nothing to do; buffers may be empty (null)
   st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
@@ -2833,6 +2906,7 @@ int moe_mxfp4_forward_ex(const moe_mxfp4_dims* dims, const void* x, const float*
                          opts ? opts->spin_limit_us : 0u);
   apply_launch(P, L);
   if (opts && (opts->flags & MOE_OPT_WITHHOLD_ARRIVAL)) P.withhold = 1;
+  if (opts && (opts->flags & MOE_OPT_WITHHOLD_H)) P.withhold_h = 1;
   if (opts && (opts->flags & MOE_OPT_TRACE))
     P.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + make_layout(dims, topk).trace);
   const int grid = grid_for(di, layer_kernel(L.v, L.mm), L.lds, opts ? opts->grid : 0);
@@ -2915,7 +2989,7 @@ int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const v
   int st = check_dims(dims, topk);
   if (st != MOE_OK) return st;
   if (layers < 1 || layers > kMaxLayers) return MOE_EINVAL;
-  if (flags & ~(MOE_LAYERS_PER_LAUNCH | MOE_LAYERS_ONE_LAUNCH)) return MOE_EINVAL;
+  if (flags & ~(MOE_LAYERS_PER_LAUNCH | MOE_LAYERS_ONE_LAUNCH | MOE_LAYERS_COOPERATIVE)) return MOE_EINVAL;
   if ((flags & MOE_LAYERS_PER_LAUNCH) && (flags & MOE_LAYERS_ONE_LAUNCH)) return MOE_EINVAL;
   if (dims->T == 0) return MOE_OK;
   st = check_ptrs(x, router_w, packed_experts, scales, out, workspace);
@@ -2936,11 +3010,14 @@ int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const v
   P.pk_stride = (size_t)dims->E * moe_mxfp4_expert_packed_bytes(dims->d, dims->ffn);
   P.sc_stride = (size_t)dims->E * moe_mxfp4_expert_scale_bytes(dims->d, dims->ffn);
   hipStream_t s = (hipStream_t)stream;
+  const bool coop = (flags & MOE_LAYERS_COOPERATIVE) != 0;
   if (flags & MOE_LAYERS_ONE_LAUNCH) {
     P.nlayers = layers;
     void* args[] = {&P};
     const int grid = grid_for(di, sk, L.lds, 0);
-    if (hipLaunchKernel(sk, dim3(grid), dim3(kWG), args, (unsigned)L.lds, s) != hipSuccess) {
+    const hipError_t e = coop ? hipLaunchCooperativeKernel(sk, dim3(grid), dim3(kWG), args, (unsigned)L.lds, s)
+                              : hipLaunchKernel(sk, dim3(grid), dim3(kWG), args, (unsigned)L.lds, s);
+    if (e != hipSuccess) {
       (void)hipGetLastError();
       return MOE_ELAUNCH;
     }
@@ -2958,7 +3035,7 @@ int moe_mxfp4_forward_layers(const moe_mxfp4_dims* dims, int32_t layers, const v
     Q.x = P.xb;
     hipLaunchKernelGGL(k_norm, dim3(dims->T), dim3(kWG), 0, s, Q);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    st = launch_layer(Q, L, grid, s, false);
+    st = launch_layer(Q, L, grid, s, coop);
     if (st != MOE_OK) return st;
   }
   return MOE_OK;

@@ -102,7 +102,7 @@ def test_layers_validation_codes(moe):
     ok_dims = (4, 64, 32, 8)
     assert _call_layers(moe, ok_dims, layers=0) == moe.MOE_EINVAL
     assert _call_layers(moe, ok_dims, layers=4097) == moe.MOE_EINVAL
-    assert _call_layers(moe, ok_dims, flags=4) == moe.MOE_EINVAL
+    assert _call_layers(moe, ok_dims, flags=8) == moe.MOE_EINVAL
     assert _call_layers(moe, ok_dims, flags=moe.MOE_LAYERS_PER_LAUNCH | moe.MOE_LAYERS_ONE_LAUNCH) == moe.MOE_EINVAL
     assert _call_layers(moe, ok_dims, x=0) == moe.MOE_EINVAL
     assert _call_layers(moe, ok_dims, topk=9) == moe.MOE_EINVAL

@@ -2,18 +2,17 @@
 top-8), in the launch configuration the benchmark times (the persistent
 single launch with its default grid).
 
-decode (T=1), verify (T=8) and verify_shared (T=8 tokens sharing most of
-their variance, so up to 7 tokens per expert): every output element against
-the oracle.
-batched_verify (T=128, Zipf-skewed routing) and dense (T=512): routing and
-permutation for all tokens, outputs for a sample of tokens (the oracle runs
-only those tokens' expert pairs).  The verify-block sweep (T = 4, 16, 22, 32)
-likewise, sampled from T = 22 on.
+Every workload: routing and permutation of every token bit for bit, and
+every output element against the oracle (no sampling): decode (T=1), verify
+(T=8), verify_shared (T=8 tokens sharing most of their variance, so up to 7
+tokens per expert), batched_verify (T=128, Zipf-skewed routing), dense
+(T=512) and the verify-block sweep (T = 4, 16, 22, 32).  For the two MFMA-path
+workloads (batched_verify, dense) also h of every expert and y of every slot.
 """
 import numpy as np
 import pytest
 
-from helpers import OUT_TOL, check_routing, rel_err, to_device
+from helpers import INTER_TOL, OUT_TOL, check_routing, rel_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -36,16 +35,13 @@ def full_env(verify_experts):
     return torch, moe, oracle, synth, p, s, pt, st
 
 
-def _run(full_env, name, sample=None):
+def _run(full_env, name, inter=False):
     torch, moe, oracle, synth, p, s, pt, st = full_env
     cfg = synth.get_config(name)
     print(f"\n[full] {name}: T={cfg.T} route_seed={cfg.route_seed}", flush=True)
     x, wr = synth.routing_inputs(cfg)
-    mask = None
-    if sample is not None:
-        mask = np.zeros(cfg.T, dtype=np.uint8)
-        mask[sample] = 1
-    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F, token_mask=mask)
+    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F, keep_intermediates=inter)
+    print(f"[full] {name}: oracle done", flush=True)
     assert ref.min_gap > 1e-3
     xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
     wrt = torch.from_numpy(wr).cuda()
@@ -56,9 +52,22 @@ def _run(full_env, name, sample=None):
     assert moe.status(ws) == moe.MOE_OK
     it = {k: v.cpu().numpy() for k, v in moe.intermediates(ws, dims, cfg.k).items()}
     check_routing(it["topk_idx"], it["topk_w"], it["offsets"], it["sorted_slot"], ref, cfg.k)
+    if inter:  # intermediates first: a failure names the step
+        worst = 0.0
+        for e in np.nonzero(np.diff(ref.offsets) > 0)[0]:
+            p0, p1 = ref.offsets[e], ref.offsets[e + 1]
+            eh = rel_err(it["h"][p0:p1], ref.h[p0:p1])
+            assert eh <= INTER_TOL, f"h of expert {e}: {eh}"
+            worst = max(worst, eh)
+        yref = np.empty_like(ref.y)
+        for slot in range(cfg.T * cfg.k):
+            t, j = divmod(slot, cfg.k)
+            yref[slot] = ref.gates[t, j] * ref.y[ref.pos[slot]]
+        ey = rel_err(it["y"], yref)
+        print(f"[full] {name}: worst h err per expert {worst:.2e}, y err {ey:.2e}", flush=True)
+        assert ey <= INTER_TOL
     got = out.cpu().numpy()
-    rows = np.arange(cfg.T) if sample is None else np.asarray(sample)
-    err = rel_err(got[rows], ref.out[rows])
+    err = rel_err(got, ref.out)
     print(f"[full] {name}: active experts {int((np.diff(ref.offsets) > 0).sum())}, out err {err:.2e}", flush=True)
     assert err <= OUT_TOL
     # staged path gives the same bits
@@ -84,13 +93,13 @@ def test_verify_shared_T8(full_env):
 
 
 def test_batched_verify_T128_zipf(full_env):
-    got, ref = _run(full_env, "batched_verify", sample=[0, 17, 40, 63, 64, 99, 127])
+    got, ref = _run(full_env, "batched_verify", inter=True)
     counts = np.diff(ref.offsets)
     assert 35 <= counts.max() <= 45 and (counts == 0).any()
 
 
 def test_dense_T512(full_env):
-    _run(full_env, "dense", sample=[0, 1, 255, 256, 300, 511])
+    _run(full_env, "dense", inter=True)
 
 
 def test_sweep_T4(full_env):
@@ -102,8 +111,8 @@ def test_sweep_T16(full_env):
 
 
 def test_sweep_T22(full_env):
-    _run(full_env, "sweep_T22", sample=[0, 7, 8, 15, 21])
+    _run(full_env, "sweep_T22")
 
 
 def test_sweep_T32(full_env):
-    _run(full_env, "sweep_T32", sample=[0, 9, 16, 30, 31])
+    _run(full_env, "sweep_T32")

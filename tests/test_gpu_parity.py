@@ -223,10 +223,37 @@ def test_watchdog_timeout_then_recovery(env):
     dims = moe.LayerDims(cfg.T, cfg.d, cfg.F, cfg.E)
     ws = moe.alloc_workspace(dims, cfg.k)
     opts = moe.Options(moe.MOE_OPT_WITHHOLD_ARRIVAL, 2000, 0)
-    moe.forward(xt, wrt, pt, st, cfg.k, workspace=ws, options=opts)
+    out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws, options=opts)
     assert moe.status(ws) == moe.MOE_ETIMEOUT
+    # no element of out was completed, and none keeps its earlier value: all NaN
+    assert torch.isnan(out).all()
     assert moe.status(ws) == moe.MOE_OK  # status is cleared by reading it
-    out = moe.forward(xt, wrt, pt, st, cfg.k, workspace=ws)
+    out = moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws)
+    assert moe.status(ws) == moe.MOE_OK
+    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
+    assert rel_err(out.cpu().numpy(), ref.out) <= OUT_TOL
+
+
+@pytest.mark.parametrize("shape", [dict(T=8, d=256, F=128, E=8, k=2), dict(T=3, d=512, F=256, E=8, k=3),
+                                   dict(T=96, d=1024, F=256, E=4, k=2)],
+                         ids=["small_path", "staged_h", "mfma_path"])
+def test_withheld_h_leaves_nan_then_recovers(env, shape):
+    # the down step waits for h words tagged for a call that never happens:
+    # every down wait is abandoned (2 ms), no y is stored, every combine wait is
+    # abandoned, so every out element is NaN; status TIMEOUT; the next normal
+    # call on the same workspace is correct
+    torch, moe, oracle, synth = env
+    cfg = synth.Config("hold_h", **shape)
+    x, wr, p, s = inputs_for(synth, cfg)
+    xt, wrt, pt, st = to_device(torch, x, wr, p, s)
+    dims = moe.LayerDims(cfg.T, cfg.d, cfg.F, cfg.E)
+    ws = moe.alloc_workspace(dims, cfg.k)
+    out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws, options=moe.Options(moe.MOE_OPT_WITHHOLD_H, 2000, 0))
+    assert moe.status(ws) == moe.MOE_ETIMEOUT
+    assert torch.isnan(out).all()
+    moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws)
     assert moe.status(ws) == moe.MOE_OK
     ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
     assert rel_err(out.cpu().numpy(), ref.out) <= OUT_TOL

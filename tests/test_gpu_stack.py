@@ -135,6 +135,7 @@ def _cfg(name, **kw):
 
 @pytest.mark.parametrize("name,kw,L", [
     ("all_x_T8", dict(T=8, d=256, F=128, E=8, k=2), 3),
+    ("all_x_T8_even", dict(T=8, d=256, F=128, E=8, k=2), 4),  # even L: layer 0 writes the workspace buffer
     ("staged_h_T1", dict(T=1, d=512, F=256, E=16, k=4), 4),
     ("two_chunks_T4", dict(T=4, d=256, F=2560, E=8, k=2), 3),
     ("all_x_T9_d7168", dict(T=9, d=7168, F=256, E=32, k=8), 3),
@@ -142,7 +143,11 @@ def _cfg(name, **kw):
 def test_one_launch_stack(name, kw, L):
     import mxfp4_moe_expert_router_amd as moe
     assert moe.layers_one_launch(moe.LayerDims(kw["T"], kw["d"], kw["F"], kw["E"]), kw["k"])
-    _run_stack(_cfg(name, **kw), L, [moe.MOE_LAYERS_ONE_LAUNCH, moe.MOE_LAYERS_PER_LAUNCH])
+    flags = [moe.MOE_LAYERS_ONE_LAUNCH, moe.MOE_LAYERS_PER_LAUNCH]
+    if name == "all_x_T8":  # both modes launched cooperatively too: the same bits
+        flags += [moe.MOE_LAYERS_ONE_LAUNCH | moe.MOE_LAYERS_COOPERATIVE,
+                  moe.MOE_LAYERS_PER_LAUNCH | moe.MOE_LAYERS_COOPERATIVE]
+    _run_stack(_cfg(name, **kw), L, flags)
 
 
 @pytest.mark.parametrize("name,kw,L", [
