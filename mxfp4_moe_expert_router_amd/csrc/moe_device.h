@@ -19,8 +19,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// E8M0 byte s -> 2^(s-127) as fp32, by placing s in the exponent field.
-// Exact for s in [1, 254]; s = 0 gives 0 and s = 255 gives +inf.
+// E8M0 byte s -> the fp32 scale operand of the scaled converts below: s in
+// the exponent field.  As an fp32 value this is 2^(s-127) for s in [1, 254]
+// and +0 for s = 0, but the converts use only the operand's exponent field,
+// so s = 0 also decodes as 2^-127 (the format's value), subnormal results
+// included (measured on MI355X for every code at s = 0, 1, 2; the GPU tests
+// check blocks of bytes 0, 1 and 254 against the oracle).  s = 255 (NaN in the
+// format) is +inf here and not supported.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __builtin_bit_cast(float, s << 23);
 }
