@@ -148,6 +148,25 @@ int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* ro
                       const uint8_t* packed_experts, const uint8_t* scales, int32_t topk,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer without a caller workspace and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments as
+ * moe_mxfp4_forward minus the workspace, the same kernels and the same result
+ * bit for bit.  The workspace is a 32 MiB array in the library's device
+ * memory, one per GPU the library runs on, held until the process ends; its
+ * address is looked up once per device, and the first call on a device
+ * enqueues a zero fill of it (a kernel) on `stream` before the layer.
+ * Sizes whose workspace (moe_mxfp4_workspace_bytes) exceeds 32 MiB are
+ * rejected with MOE_EWORKSPACE: e.g. every T <= 32 at d = 7168, ffn = 2048,
+ * E = 256, top-8 fits, T = 64 does not.  Every call on a GPU shares that GPU's
+ * array: calls that may overlap on one GPU (two streams, two threads) race and
+ * must not be made.  A timed-out call leaves NaN in out as moe_mxfp4_forward
+ * does (its status word is not readable: there is no workspace pointer).
+ * Errors: as moe_mxfp4_forward (no workspace arguments to check). */
+int moe_mxfp4_forward_noalloc(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                              const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                              void* stream);
+
 /* Same layer and the same result bit for bit, as one kernel launch per step
  * ([P5-TRT]'s per-operator model), for measuring what the single launch saves. */
 int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const float* router_w,

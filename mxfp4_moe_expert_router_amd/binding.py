@@ -68,6 +68,8 @@ def _load():
     lib.moe_mxfp4_forward.argtypes = fwd + [vp]
     lib.moe_mxfp4_forward_staged.restype = ctypes.c_int
     lib.moe_mxfp4_forward_staged.argtypes = fwd + [vp]
+    lib.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_noalloc.argtypes = [P(Dims), vp, vp, vp, vp, i32, vp, vp]
     lib.moe_mxfp4_forward_ex.restype = ctypes.c_int
     lib.moe_mxfp4_forward_ex.argtypes = fwd + [P(Options), vp]
     lib.moe_mxfp4_route.restype = ctypes.c_int
@@ -211,6 +213,19 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor, scale
     else:
         st = lib.moe_mxfp4_forward(*args, _stream(stream))
     _check(st, "moe_mxfp4_forward" + ("_staged" if staged else ""))
+    return out
+
+
+def forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                    topk: int, out: torch.Tensor, stream=None, dims: Optional[LayerDims] = None) -> torch.Tensor:
+    """One MoE layer on the library's own device workspace
+    (moe_mxfp4_forward_noalloc): nothing is allocated; `out` fp32 [T, d] is
+    the caller's."""
+    dims = dims or dims_of(x, router_w, packed)
+    _validate(x, router_w, packed, scales, out, dims)
+    st = lib.moe_mxfp4_forward_noalloc(ctypes.byref(dims.c()), _ptr(x), _ptr(router_w), _ptr(packed), _ptr(scales),
+                                       int(topk), _ptr(out), _stream(stream))
+    _check(st, "moe_mxfp4_forward_noalloc")
     return out
 
 

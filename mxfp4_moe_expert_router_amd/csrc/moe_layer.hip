@@ -925,10 +925,9 @@ struct GURow {
 
 // Loads are unconditional (no divergent branch between them, so they all stay
 // in flight): a lane past the end of the row re-reads the row's last chunk
-// with its scale byte masked to 0, i.e. 2^-127 (the convert takes the scale's
-// exponent; an fp32 0 is exponent 0).  Its 32 terms then add less than 2^-110
-// for |x| < 2^8, below half an ulp of any fp32 sum above 2^-86 in magnitude:
-// they do not change g or u.  (Zeroing the codes instead cost 2% of the
+// with its scale byte masked to 0, which decodes as 2^-127 (see e8m0_to_f32).
+// Its 32 terms then add less than 2^-110 for |x| < 2^8, below half an ulp of
+// any fp32 sum above 2^-86 in magnitude: they do not change g or u.  (Zeroing the codes instead cost 2% of the
 // verify layer's time.)
 __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho, GURow& R) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -2656,11 +2655,20 @@ static int device_info(DeviceInfo* out) {
   return MOE_OK;
 }
 
+static int check_io_ptrs(const void* x, const float* wr, const uint8_t* packed, const uint8_t* scales,
+                         const float* out) {
+  if (!x || !wr || !packed || !scales || !out) return MOE_EINVAL;
+  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
+  if (!al(x, 16) || !al(wr, 16) || !al(packed, 16) || !al(out, 16)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
 static int check_ptrs(const void* x, const float* wr, const uint8_t* packed, const uint8_t* scales, const float* out,
                       const void* ws) {
-  if (!x || !wr || !packed || !scales || !out || !ws) return MOE_EINVAL;
-  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
-  if (!al(x, 16) || !al(wr, 16) || !al(packed, 16) || !al(out, 16) || !al(ws, kAlign)) return MOE_EALIGN;
+  const int st = check_io_ptrs(x, wr, packed, scales, out);
+  if (st != MOE_OK) return st;
+  if (!ws) return MOE_EINVAL;
+  if ((uintptr_t)ws % kAlign) return MOE_EALIGN;
   return MOE_OK;
 }
 
@@ -2820,6 +2828,46 @@ static int launch_staged(const Params& P, const Launch& L, int grid, hipStream_t
   return MOE_OK;
 }
 
+// ------------------------------------------------- allocation-free calls ---
+// moe_mxfp4_forward_noalloc runs the layer on a workspace that is a
+// file-scope device array instead of a caller buffer.  Each device the
+// library runs on holds its own copy (kScratchBytes) until the process ends.
+// In host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchInfo {
+  void* ptr = nullptr;
+  bool cleared = false;
+};
+static ScratchInfo g_scratch[64];
+
+// This device's scratch address (set up on first use, with the device
+// current); the first call also enqueues a zero fill of it on `s`, ahead of
+// the layer kernel that will use it.
+static int scratch_for_device(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  ScratchInfo& si = g_scratch[dev];
+  if (si.ptr == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return MOE_EDEVICE;
+    }
+    si.ptr = ptr;
+  }
+  if (!si.cleared) {
+    hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(si.ptr), kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    si.cleared = true;
+  }
+  *out = si.ptr;
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -2918,6 +2966,24 @@ int moe_mxfp4_forward(const moe_mxfp4_dims* dims, const void* x, const float* ro
                       void* workspace, size_t workspace_bytes, void* stream) {
   return moe_mxfp4_forward_ex(dims, x, router_w, packed_experts, scales, topk, out, workspace, workspace_bytes,
                               nullptr, stream);
+}
+
+int moe_mxfp4_forward_noalloc(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
+                              const uint8_t* packed_experts, const uint8_t* scales, int32_t topk, float* out,
+                              void* stream) {
+  int st = check_dims(dims, topk);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  const size_t need = make_layout(dims, topk).total;
+  if (need > kScratchBytes) return MOE_EWORKSPACE;
+  // the pointers are checked before the scratch is set up (which may enqueue
+  // its first zero fill)
+  st = check_io_ptrs(x, router_w, packed_experts, scales, out);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_device((hipStream_t)stream, &ws);
+  if (st != MOE_OK) return st;
+  return moe_mxfp4_forward_ex(dims, x, router_w, packed_experts, scales, topk, out, ws, need, nullptr, stream);
 }
 
 int moe_mxfp4_forward_staged(const moe_mxfp4_dims* dims, const void* x, const float* router_w,
