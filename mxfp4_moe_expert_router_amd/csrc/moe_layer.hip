@@ -200,13 +200,14 @@ struct Smem {
   int* cdn;   // [n_active + 1] same for down
   float* rt;  // router_mfma's partial tiles (more than kRouterMfmaT tokens)
   int* misc;  // [0] n_active, [1] / [2] work counters, [8..8+kWaves) scan scratch, [16..50) round tables,
-              // [50] / [51] staged x rows (xmode 1)
+              // [50] / [51] staged x rows (xmode 1), [52] MFMA unit stride
 };
 
 // Round table of the small-batch expert steps (phase 0 gate/up, 1 down) in
 // S.misc: kRounds chunk starts, then kRounds + 1 cumulative chunk lengths.
 constexpr int kRoundTab = 2 * kRounds + 1;
 constexpr int kMiscXBase = 50, kMiscXRows = 51;  // x rows staged in LDS (xmode 1): first pair, count
+constexpr int kMiscStride = 52;                  // MFMA path: stride between a workgroup's units
 __device__ __forceinline__ int* round_tab(const Smem& S, int phase) { return S.misc + 16 + phase * kRoundTab; }
 
 __device__ __forceinline__ Smem carve(char* base, const Params& P, bool small) {
@@ -1464,25 +1465,36 @@ __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, ui
 //    workgroup, so a wave rarely needs a new h).  Work tables in round_tab;
 //    S.misc[1] / [2] = 0: gate/up and down counters over the workgroup's
 //    chunks.
-//  - MFMA path: one contiguous range per list: S.misc[5] / [3] = gate/up start
-//    and end (S.misc[1] its counter), S.misc[6] / [4] = down start and end
-//    (S.misc[2]).
+//  - MFMA path: per list, units U0, U0 + stride, ... below U1: S.misc[5] /
+//    [3] = gate/up U0 and U1 (S.misc[1] its counter), S.misc[6] / [4] = down
+//    U0 and U1 (S.misc[2]), S.misc[kMiscStride] = the stride (see below).
 // All threads; ends with a barrier.
 __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int wg, int G) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int na = S.misc[0];
   if (P.mfma) {
-    if (wave < 4) {  // waves 0-3: gate/up start and end, down start and end
+    // Workgroups are dealt to the XCDs in turn (wg % 8 on XCD wg % 8), each
+    // XCD with its own L2.  Each list is cut into one chunk of equal modelled
+    // work per XCD, and a chunk's units are dealt to the XCD's workgroups in
+    // turn (workgroup j of the XCD takes units j, j + per, ...): at any time
+    // the XCD's workgroups work on the units of two or three experts, whose
+    // activation tiles (x of the experts' tokens, h) then stay in its L2
+    // instead of being fetched again for each unit (measured at T=512 with
+    // contiguous per-workgroup ranges: 32 experts' x per XCD, twice the L2).
+    const int nx = (G % 8 == 0 && G >= 16) ? 8 : 1;
+    const int per = G / nx, xcd = wg % nx, j = wg / nx;
+    if (wave < 4) {  // waves 0-3: gate/up chunk start and end, down chunk start and end
       const bool gu = wave < 2;
       const int R = gu ? (P.F + kGUUnitRows - 1) / kGUUnitRows : (P.d + kDnUnitRows - 1) / kDnUnitRows;
-      const int v = row_at(gu ? S.cgu : S.cdn, na, R, wg + (wave & 1), G);
+      const int v = row_at(gu ? S.cgu : S.cdn, na, R, xcd + (wave & 1), nx);
       if (lane == 0) {
-        if (wave == 0) S.misc[1] = S.misc[5] = v;
+        if (wave == 0) S.misc[1] = S.misc[5] = v + j;
         if (wave == 1) S.misc[3] = v;
-        if (wave == 2) S.misc[2] = S.misc[6] = v;
+        if (wave == 2) S.misc[2] = S.misc[6] = v + j;
         if (wave == 3) S.misc[4] = v;
       }
     }
+    if (threadIdx.x == 0) S.misc[kMiscStride] = per;
     __syncthreads();
     return;
   }
@@ -1571,14 +1583,16 @@ __device__ __forceinline__ void seg_next(const Smem& S, int U1, int R, int nkb, 
   c.j = 0;
   c.pass += pass_len;
   if (c.pass < c.ne) return;
-  if (c.u + 1 < U1) seg_unit(S, c.u + 1, R, c);
+  const int st = uni(S.misc[kMiscStride]);
+  if (c.u + st < U1) seg_unit(S, c.u + st, R, c);
   else c.valid = false;
 }
 
-// Number of positions (unit, pass, K block) in units [U0, U1).
+// Number of positions (unit, pass, K block) in units U0, U0 + stride, ... < U1.
 __device__ __forceinline__ int seg_count(const Smem& S, int U0, int U1, int R, int nkb, int pass_len) {
   int n = 0;
-  for (int u = U0; u < U1; ++u) {
+  const int st = uni(S.misc[kMiscStride]);
+  for (int u = U0; u < U1; u += st) {
     const int e = uni(S.act[u / R]);
     const int ne = uni(S.off[e + 1]) - uni(S.off[e]);
     n += (ne + pass_len - 1) / pass_len;
@@ -1672,7 +1686,7 @@ __device__ __forceinline__ void gu_mfma_xload(const Params& P, const Smem& S, co
                                               u32x4_t (&v)[kXPieces], uint32_t& ok) {
   const int TK = P.T * P.k;
   const int np = min(kGUPass, c.ne - c.pass);
-  const int tok = uni(S.slot[min(c.p0 + c.pass, TK - 1)]) / P.k;  // a valid row for the clamped reads
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x, (uint32_t)((size_t)P.T * P.d * 2));
   ok = 0;
 #pragma unroll
   for (int m = 0; m < kXPieces; ++m) {
@@ -1680,8 +1694,11 @@ __device__ __forceinline__ void gu_mfma_xload(const Params& P, const Smem& S, co
     const int n = pc >> 6, b = (pc >> 4) & 3, q = pc & 15;
     const int kk = (c.j * kGUK + b) * kKB + 8 * q;
     const bool use = c.valid && n < np && kk < P.d;
-    const int t = use ? S.slot[min(c.p0 + c.pass + n, TK - 1)] / P.k : tok;
-    v[m] = *reinterpret_cast<const u32x4_t*>(P.x + (size_t)t * P.d + min(kk, P.d - 8));
+    // pieces past the pass's tokens or past d read past the descriptor's
+    // end: no memory access, zeros (and they are written as zeros)
+    const int t = S.slot[min(c.p0 + c.pass + n, TK - 1)] / P.k;
+    const uint32_t off = use ? (uint32_t)(((size_t)t * P.d + kk) * 2) : 0xFFFFFFF0u;
+    v[m] = ld_cached16(xr, off);
     ok |= use ? 1u << m : 0u;
   }
 }
@@ -1755,16 +1772,19 @@ __device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int
   }
 }
 
-// One step: prefetch the next step (x tile into registers, weights into An),
-// compute the current one (Ac, LDS tile `cur`), write the next tile into LDS
-// tile `nxt`, synchronise.  Returns false when the stream is done.
+// One step q: prefetch the x tile of step q + 1 into registers (n1) and the
+// weights of step q + 2 (n2, into An2), compute step q (weights Ac, LDS tile
+// `cur`), write tile q + 1 into LDS tile `nxt`, synchronise.  The weights are
+// in flight for two steps: with one step, a step's loads were waited for at
+// the next step (a step's compute and the x tile take less than one loaded
+// memory latency).
 __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
-                                            int q, int npos, Seg& cc, Seg& nc, const GUA& Ac, GUA& An, char* cur,
-                                            char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
+                                            int q, int npos, Seg& cc, Seg& n1, Seg& n2, const GUA& Ac, GUA& An2,
+                                            char* cur, char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
   u32x4_t xr[kXPieces];
   uint32_t xok;
-  gu_mfma_xload(P, S, nc, xr, xok);  // first: waiting for it below must not wait for An
-  gu_mfma_load(P, nc, R, An);
+  gu_mfma_xload(P, S, n1, xr, xok);  // first: waiting for it below must not wait for An2
+  gu_mfma_load(P, n2, R, An2);
   if (cc.ne - cc.pass > 16)
     gu_mfma_step<2>(Ac, cur, ag, au);
   else
@@ -1772,40 +1792,55 @@ __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint
   if (cc.j == nst - 1) gu_mfma_store(P, cc, R, tag, ag, au);
   if (q + 1 < npos) gu_mfma_xstore(nxt, xr, xok);
   seg_next(S, U1, R, nst, kGUPass, cc);
-  seg_next(S, U1, R, nst, kGUPass, nc);
+  seg_next(S, U1, R, nst, kGUPass, n1);
+  seg_next(S, U1, R, nst, kGUPass, n2);
   lds_barrier();
 }
 
 // Gate/up + SwiGLU for the workgroup's units [U0, U1) (equal shares of the
-// modelled work).  All threads of the workgroup.
+// modelled work).  All threads of the workgroup.  Three weight buffers
+// (steps q, q + 1, q + 2), two LDS x tiles.
 __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int R = (P.F + kGUUnitRows - 1) / kGUUnitRows;
   const int nst = (P.d + kGUK * kKB - 1) / (kGUK * kKB);
   const int U0 = uni(S.misc[5]), U1 = uni(S.misc[3]);
   const int npos = seg_count(S, U0, U1, R, nst, kGUPass);
   if (npos == 0) return;
-  char* t0 = reinterpret_cast<char*>(S.xs);
-  char* t1 = t0 + kGUK * kGUPass * kTileRow;
-  Seg cc, nc;
+  char* cur = reinterpret_cast<char*>(S.xs);
+  char* nxt = cur + kGUK * kGUPass * kTileRow;
+  Seg cc, n1, n2;
   seg_start(S, U0, U1, R, cc);
-  nc = cc;
-  GUA A0, A1;
+  n1 = cc;
+  seg_next(S, U1, R, nst, kGUPass, n1);
+  n2 = n1;
+  seg_next(S, U1, R, nst, kGUPass, n2);
+  GUA A0, A1, A2;
   f32x4_t ag[2], au[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) ag[g] = au[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
     u32x4_t xr[kXPieces];
     uint32_t xok;
-    gu_mfma_xload(P, S, nc, xr, xok);
-    gu_mfma_load(P, nc, R, A0);
-    gu_mfma_xstore(t0, xr, xok);
-    seg_next(S, U1, R, nst, kGUPass, nc);
+    gu_mfma_xload(P, S, cc, xr, xok);
+    gu_mfma_load(P, cc, R, A0);
+    gu_mfma_load(P, n1, R, A1);
+    gu_mfma_xstore(cur, xr, xok);
     lds_barrier();
   }
-  for (int q = 0; q < npos; q += 2) {
-    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, nc, A0, A1, t0, t1, ag, au);
+  const auto swap_tiles = [&] {
+    char* t = cur;
+    cur = nxt;
+    nxt = t;
+  };
+  for (int q = 0; q < npos; q += 3) {
+    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, A0, A2, cur, nxt, ag, au);
     if (q + 1 >= npos) break;
-    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, nc, A1, A0, t1, t0, ag, au);
+    swap_tiles();
+    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, A1, A0, cur, nxt, ag, au);
+    if (q + 2 >= npos) break;
+    swap_tiles();
+    gu_mfma_one(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, A2, A1, cur, nxt, ag, au);
+    swap_tiles();
   }
 }
 
@@ -1872,12 +1907,15 @@ constexpr int kHPieces = kDnPass * kHRow / kWG;
 template <bool COHERENT>
 __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
                                               u32x4_t (&v)[kHPieces]) {
-  const int np = max(1, min(kDnPass, c.ne - c.pass));
+  const int np = min(kDnPass, c.ne - c.pass);
 #pragma unroll
   for (int m = 0; m < kHPieces; ++m) {
     const int pc = (int)threadIdx.x + kWG * m;
-    const int n = min(pc / kHRow, np - 1), k = min(c.j * kDnK * kKB + 2 * (pc % kHRow), P.F - 2);
-    const uint32_t off = ((uint32_t)(c.p0 + c.pass + n) * (uint32_t)P.F + (uint32_t)k) * 8u;
+    const int n = pc / kHRow, k = c.j * kDnK * kKB + 2 * (pc % kHRow);
+    // pieces past the pass's pairs or past F read past the descriptor's end:
+    // no memory access, zeros (dn_mfma_hstore neither checks nor uses them)
+    const bool use = c.valid && n < np && k < P.F;
+    const uint32_t off = use ? ((uint32_t)(c.p0 + c.pass + n) * (uint32_t)P.F + (uint32_t)k) * 8u : 0xFFFFFFF0u;
     v[m] = COHERENT ? ld_coherent16(rs, off) : ld_cached16(rs, off);
   }
 }
@@ -2082,50 +2120,107 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite f
 }
-__device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW, int layer) {
+// The k gated rows of unit u's token at the unit's columns (16-byte loads of
+// two tagged words per lane), summed in slot order.  The loads of all k slots,
+// of up to two units (U units), are issued before any is used (groups of 8
+// slots), so a wave waits for one round trip per group instead of one per
+// slot.  ok[i]: every word of unit i carried the call's tag.
+constexpr int kCombCols = 2 * kWave;  // two columns (one 16-byte load of tagged words) per lane
+template <int U>
+__device__ __forceinline__ void combine_sum(const Params& P, uint32_t tag, const int (&u)[U], int nd, float (&a0)[U],
+                                            float (&a1)[U], bool (&ok)[U]) {
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kCols = 2 * kWave;  // two columns (one 16-byte load of tagged words) per lane
-  const int nd = (P.d + kCols - 1) / kCols;
-  const int nunits = P.T * nd;
-  for (int u = gw; u < nunits; u += NW) {
-    const int t = u / nd, c = (u % nd) * kCols + 2 * lane;  // d is even: c < d means c + 1 < d
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.yq + (size_t)t * P.k * P.d, (uint32_t)(P.k * P.d) * 8u);
-    const uint64_t t0 = wall_clock64();
-  int round = 0;
-    for (;;) {
-      bool ok = true;
-      float a0 = 0.f, a1 = 0.f;
-      const uint32_t cc = (uint32_t)min(c, P.d - 2);
-      for (int j = 0; j < P.k; ++j) {
-        const u32x4_t q = ld_coherent16(rs, ((uint32_t)j * P.d + cc) * 8u);
-        ok &= (q.y == tag) && (q.w == tag);
-        a0 += u2f(q.x);
-        a1 += u2f(q.z);
-      }
-      if (__all(ok)) {
-        if (c < P.d) {
-          float2* o = reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c);
-          if (P.stack_layers > 0) {  // uniform
-            if (layer == 0) {
-              const uint32_t xv = *reinterpret_cast<const uint32_t*>(P.x0 + (size_t)t * P.d + c);
-              a0 = bf16lo(xv) + a0;
-              a1 = bf16hi(xv) + a1;
-            } else {
-              const float2 r = *reinterpret_cast<const float2*>(P.rin + (size_t)t * P.d + c);
-              a0 = r.x + a0;
-              a1 = r.y + a1;
-            }
-            o = reinterpret_cast<float2*>(P.rout + (size_t)t * P.d + c);
-            const uint64_t bits = (uint64_t)__builtin_bit_cast(uint32_t, a0) |
-                                  ((uint64_t)__builtin_bit_cast(uint32_t, a1) << 32);
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(o), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            *o = make_float2(a0, a1);
-          }
+  __amdgpu_buffer_rsrc_t rs[U];
+  uint32_t cc[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int t = u[i] / nd, c = (u[i] % nd) * kCombCols + 2 * lane;  // d is even: c < d means c + 1 < d
+    rs[i] = make_rsrc(P.yq + (size_t)t * P.k * P.d, (uint32_t)(P.k * P.d) * 8u);
+    cc[i] = (uint32_t)min(c, P.d - 2);
+    a0[i] = a1[i] = 0.f;
+    ok[i] = true;
+  }
+  for (int j0 = 0; j0 < P.k; j0 += 8) {
+    u32x4_t q[U][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < P.k)  // uniform
+#pragma unroll
+        for (int i = 0; i < U; ++i) q[i][j] = ld_coherent16(rs[i], ((uint32_t)(j0 + j) * P.d + cc[i]) * 8u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < P.k)
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+          ok[i] &= (q[i][j].y == tag) && (q[i][j].w == tag);
+          a0[i] += u2f(q[i][j].x);
+          a1[i] += u2f(q[i][j].z);
         }
-        break;
+  }
+}
+
+// Writes unit u's sums (see combine_step).
+__device__ __forceinline__ void combine_store(const Params& P, int u, int nd, int layer, float a0, float a1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = u / nd, c = (u % nd) * kCombCols + 2 * lane;
+  if (c >= P.d) return;
+  float2* o = reinterpret_cast<float2*>(P.out + (size_t)t * P.d + c);
+  if (P.stack_layers > 0) {  // uniform
+    if (layer == 0) {
+      const uint32_t xv = *reinterpret_cast<const uint32_t*>(P.x0 + (size_t)t * P.d + c);
+      a0 = bf16lo(xv) + a0;
+      a1 = bf16hi(xv) + a1;
+    } else {
+      const float2 r = *reinterpret_cast<const float2*>(P.rin + (size_t)t * P.d + c);
+      a0 = r.x + a0;
+      a1 = r.y + a1;
+    }
+    o = reinterpret_cast<float2*>(P.rout + (size_t)t * P.d + c);
+    const uint64_t bits =
+        (uint64_t)__builtin_bit_cast(uint32_t, a0) | ((uint64_t)__builtin_bit_cast(uint32_t, a1) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(o), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *o = make_float2(a0, a1);
+  }
+}
+
+// Unit u until its words are current (polling with the watchdog), then stored.
+__device__ __forceinline__ bool combine_wait(const Params& P, uint32_t tag, int u, int nd, int layer) {
+  const uint64_t t0 = wall_clock64();
+  int round = 0;
+  for (;;) {
+    const int uu[1] = {u};
+    float a0[1], a1[1];
+    bool ok[1];
+    combine_sum<1>(P, tag, uu, nd, a0, a1, ok);
+    if (__all(ok[0])) {
+      combine_store(P, u, nd, layer, a0[0], a1[0]);
+      return true;
+    }
+    if (!keep_waiting(P, tag, t0, kSiteY, u, round, 3)) return false;
+  }
+}
+
+__device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int gw, int NW, int layer) {
+  const int nd = (P.d + kCombCols - 1) / kCombCols;
+  const int nunits = P.T * nd;
+  // units gw, gw + NW, ... taken two at a time: one first attempt for both,
+  // then whichever is not complete waits on its own
+  for (int u = gw; u < nunits; u += 2 * NW) {
+    if (u + NW < nunits) {  // uniform
+      const int uu[2] = {u, u + NW};
+      float a0[2], a1[2];
+      bool ok[2];
+      combine_sum<2>(P, tag, uu, nd, a0, a1, ok);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (__all(ok[i]))
+          combine_store(P, uu[i], nd, layer, a0[i], a1[i]);
+        else if (!combine_wait(P, tag, uu[i], nd, layer))
+          return false;
       }
-      if (!keep_waiting(P, tag, t0, kSiteY, u, round, 3)) return false;
+    } else if (!combine_wait(P, tag, u, nd, layer)) {
+      return false;
     }
   }
   return true;
@@ -2139,11 +2234,10 @@ __device__ __forceinline__ bool combine_step(const Params& P, uint32_t tag, int 
 // whose wait was abandoned stores no tagged results.
 __device__ __forceinline__ void poison_out(const Params& P, float* dst, int gw, int NW) {
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kCols = 2 * kWave;
-  const int nd = (P.d + kCols - 1) / kCols;
+  const int nd = (P.d + kCombCols - 1) / kCombCols;
   const float nan = __builtin_nanf("");
   for (int u = gw; u < P.T * nd; u += NW) {
-    const int t = u / nd, c = (u % nd) * kCols + 2 * lane;
+    const int t = u / nd, c = (u % nd) * kCombCols + 2 * lane;
     if (c < P.d) *reinterpret_cast<float2*>(dst + (size_t)t * P.d + c) = make_float2(nan, nan);
   }
 }
