@@ -354,6 +354,15 @@ __device__ __forceinline__ u32x4_t ld_cached16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// 16-byte streaming load (nt: read once) and byte load through a buffer
+// descriptor, at a 32-bit byte offset.
+__device__ __forceinline__ u32x4_t ld_stream16_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
+}
+__device__ __forceinline__ uint32_t ld_byte_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, byte_off, 0, 0);
+}
+
 // Drops this XCD's L2 lines (and the CU's vector cache), so that later cached
 // reads of the workspace fetch what the other XCDs wrote through to memory.
 // Issued without a wait: later waits of the wave cover it.

@@ -1631,18 +1631,23 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = d / 32;
   const int r0 = (c.u % R) * kGUUnitRows + 16 * wave;
-  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
-  const uint8_t* pe = P.packed + (size_t)c.e * pbytes;
-  const uint8_t* se = P.scales + (size_t)c.e * sbytes;
+  // one expert's codes and scales through buffer descriptors: 32-bit offsets
+  // (an expert is at most 3 * 8192 * 4096 / 2 bytes)
+  const uint32_t pbytes = (uint32_t)(3 * d / 2) * (uint32_t)F, sbytes = (uint32_t)(3 * NCH) * (uint32_t)F;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.packed + (size_t)c.e * pbytes, pbytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(P.scales + (size_t)c.e * sbytes, sbytes);
+  const uint32_t up = (uint32_t)F * (uint32_t)(d / 2), sup = (uint32_t)F * (uint32_t)NCH;
   A.keep = 0;
 #pragma unroll
   for (int i = 0; i < kGUK; ++i) {
     const int rr = min(r0 + 8 * (i & 1) + (lane >> 3), F - 1);
     const int cc = min(16 * c.j + 8 * (i >> 1) + (lane & 7), NCH - 1);
-    A.g[i] = ld_stream16(pe + (size_t)rr * (d / 2) + (size_t)cc * 16);
-    A.u[i] = ld_stream16(pe + (size_t)F * d / 2 + (size_t)rr * (d / 2) + (size_t)cc * 16);
-    A.sg[i] = se[(size_t)rr * NCH + cc];
-    A.su[i] = se[(size_t)F * NCH + (size_t)rr * NCH + cc];
+    const uint32_t po = (uint32_t)rr * (uint32_t)(d / 2) + (uint32_t)cc * 16u;
+    const uint32_t so = (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc;
+    A.g[i] = ld_stream16_buf(pr, po);
+    A.u[i] = ld_stream16_buf(pr, po + up);
+    A.sg[i] = ld_byte_buf(sr, so);
+    A.su[i] = ld_byte_buf(sr, so + sup);
     // in range, for the MFMA-layout chunk this lane will hold for block i
     const int row = r0 + (lane & 15), ch = 16 * c.j + 4 * i + (lane >> 4);
     A.keep |= (row < F && ch < NCH) ? 1u << i : 0u;
@@ -1650,7 +1655,13 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
 }
 // K block b of the MFMA layout from the loads: lane l = 16 h + r takes chunk
 // 4 b + h of row r, held by load 2 (b >> 1) + (r >> 3) of lane
-// 8 (r & 7) + 4 (b & 1) + h.
+// 8 (r & 7) + 4 (b & 1) + h.  The permute's sources s and s + 32 share an LDS
+// bank (two-way conflicts: ~19% of the step's cycles stall on them), but the
+// load order that avoids them costs more: measured at T=512, loads with rows
+// varying fastest across the lanes made the gate/up step 11% slower and loads
+// with the chunks of a line rotated by the row 2% slower (the address
+// processing of the loads backs up when consecutive lanes do not read
+// consecutive bytes), the conflicts falling to 7% either way.
 __device__ __forceinline__ uint32_t bperm(uint32_t v, int addr) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
 }
@@ -1682,23 +1693,37 @@ __device__ __forceinline__ void gu_mfma_take(const GUA& A, int b, u32x4_t& g, u3
 // `ok` bit m marks pieces that hold data (others are written as zeros).
 constexpr int kXPieces = kGUK * kGUPass * 16 / kWG;
 static_assert(kGUK == 4 && kXPieces == 4, "piece index = token(5) | block(2) | piece(4) bits");
-__device__ __forceinline__ void gu_mfma_xload(const Params& P, const Smem& S, const Seg& c,
+// Token rows of the x tile pieces a thread loads: piece m of thread i is
+// token n = i / 64 + 8 m of the pass (the same for the whole wave), K element
+// 128 b + 8 q of the step's 512 (b = (i / 16) % 4, q = i % 16).  The rows
+// (token * d) change only with the pass, so they are looked up once per pass
+// (key: the pass's first pair).
+struct XRows {
+  int key;
+  int row[kXPieces];
+};
+__device__ __forceinline__ void gu_mfma_xload(const Params& P, const Smem& S, const Seg& c, XRows& xr,
                                               u32x4_t (&v)[kXPieces], uint32_t& ok) {
   const int TK = P.T * P.k;
   const int np = min(kGUPass, c.ne - c.pass);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x, (uint32_t)((size_t)P.T * P.d * 2));
+  const int wave = threadIdx.x / kWave;
+  const __amdgpu_buffer_rsrc_t xd = make_rsrc(P.x, (uint32_t)((size_t)P.T * P.d * 2));
+  const int key = c.p0 + c.pass;
+  if (c.valid && key != xr.key) {  // uniform
+    xr.key = key;
+#pragma unroll
+    for (int m = 0; m < kXPieces; ++m)
+      xr.row[m] = uni(S.slot[min(key + wave + 8 * m, TK - 1)] / P.k) * P.d;
+  }
+  const int kk = c.j * (kGUK * kKB) + (((int)threadIdx.x >> 4) & 3) * kKB + 8 * ((int)threadIdx.x & 15);
   ok = 0;
 #pragma unroll
   for (int m = 0; m < kXPieces; ++m) {
-    const int pc = (int)threadIdx.x + kWG * m;
-    const int n = pc >> 6, b = (pc >> 4) & 3, q = pc & 15;
-    const int kk = (c.j * kGUK + b) * kKB + 8 * q;
-    const bool use = c.valid && n < np && kk < P.d;
+    const bool use = c.valid && wave + 8 * m < np && kk < P.d;
     // pieces past the pass's tokens or past d read past the descriptor's
     // end: no memory access, zeros (and they are written as zeros)
-    const int t = S.slot[min(c.p0 + c.pass + n, TK - 1)] / P.k;
-    const uint32_t off = use ? (uint32_t)(((size_t)t * P.d + kk) * 2) : 0xFFFFFFF0u;
-    v[m] = ld_cached16(xr, off);
+    const uint32_t off = use ? (uint32_t)(xr.row[m] + kk) * 2u : 0xFFFFFFF0u;
+    v[m] = ld_cached16(xd, off);
     ok |= use ? 1u << m : 0u;
   }
 }
@@ -1779,18 +1804,18 @@ __device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int
 // the next step (a step's compute and the x tile take less than one loaded
 // memory latency).
 __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
-                                            int q, int npos, Seg& cc, Seg& n1, Seg& n2, const GUA& Ac, GUA& An2,
-                                            char* cur, char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
-  u32x4_t xr[kXPieces];
+                                            int q, int npos, Seg& cc, Seg& n1, Seg& n2, XRows& xrows, const GUA& Ac,
+                                            GUA& An2, char* cur, char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
+  u32x4_t xv[kXPieces];
   uint32_t xok;
-  gu_mfma_xload(P, S, n1, xr, xok);  // first: waiting for it below must not wait for An2
+  gu_mfma_xload(P, S, n1, xrows, xv, xok);  // first: waiting for it below must not wait for An2
   gu_mfma_load(P, n2, R, An2);
   if (cc.ne - cc.pass > 16)
     gu_mfma_step<2>(Ac, cur, ag, au);
   else
     gu_mfma_step<1>(Ac, cur, ag, au);
   if (cc.j == nst - 1) gu_mfma_store(P, cc, R, tag, ag, au);
-  if (q + 1 < npos) gu_mfma_xstore(nxt, xr, xok);
+  if (q + 1 < npos) gu_mfma_xstore(nxt, xv, xok);
   seg_next(S, U1, R, nst, kGUPass, cc);
   seg_next(S, U1, R, nst, kGUPass, n1);
   seg_next(S, U1, R, nst, kGUPass, n2);
@@ -1818,13 +1843,15 @@ __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uin
   f32x4_t ag[2], au[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) ag[g] = au[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  XRows xrows;
+  xrows.key = -1;
   {
-    u32x4_t xr[kXPieces];
+    u32x4_t xv[kXPieces];
     uint32_t xok;
-    gu_mfma_xload(P, S, cc, xr, xok);
+    gu_mfma_xload(P, S, cc, xrows, xv, xok);
     gu_mfma_load(P, cc, R, A0);
     gu_mfma_load(P, n1, R, A1);
-    gu_mfma_xstore(cur, xr, xok);
+    gu_mfma_xstore(cur, xv, xok);
     lds_barrier();
   }
   const auto swap_tiles = [&] {
@@ -1833,13 +1860,13 @@ __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uin
     nxt = t;
   };
   for (int q = 0; q < npos; q += 3) {
-    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, A0, A2, cur, nxt, ag, au);
+    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, xrows, A0, A2, cur, nxt, ag, au);
     if (q + 1 >= npos) break;
     swap_tiles();
-    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, A1, A0, cur, nxt, ag, au);
+    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, xrows, A1, A0, cur, nxt, ag, au);
     if (q + 2 >= npos) break;
     swap_tiles();
-    gu_mfma_one(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, A2, A1, cur, nxt, ag, au);
+    gu_mfma_one(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, xrows, A2, A1, cur, nxt, ag, au);
     swap_tiles();
   }
 }
@@ -1860,17 +1887,19 @@ static_assert(kDnK == 2, "a step covers one 128-byte line (8 chunks) of each W_d
 __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int R, DnA& A) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = F / 32;
-  const size_t pbytes = (size_t)3 * d * F / 2, sbytes = (size_t)3 * d * F / 32;
-  const uint8_t* pd = P.packed + (size_t)c.e * pbytes + (size_t)F * d;
-  const uint8_t* sd = P.scales + (size_t)c.e * sbytes + (size_t)F * d / 16;
+  // W_down of one expert through buffer descriptors (32-bit offsets)
+  const uint32_t pbytes = (uint32_t)(3 * d / 2) * (uint32_t)F, sbytes = (uint32_t)(3 * d / 32) * (uint32_t)F;
+  const uint32_t dn = (uint32_t)F * (uint32_t)d;  // W_down after W_gate and W_up
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(P.packed + (size_t)c.e * pbytes + dn, dn / 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(P.scales + (size_t)c.e * sbytes + dn / 16, dn / 32);
   const int r0 = (c.u % R) * kDnUnitRows + 64 * wave;
+  const int cc = min(8 * c.j + (lane & 7), NCH - 1);
   A.keep = 0;
 #pragma unroll
   for (int i = 0; i < kDnK * kDnTiles; ++i) {
     const int rr = min(r0 + 8 * i + (lane >> 3), d - 1);
-    const int cc = min(8 * c.j + (lane & 7), NCH - 1);
-    A.w[i] = ld_stream16(pd + (size_t)rr * (F / 2) + (size_t)cc * 16);
-    A.s[i] = sd[(size_t)rr * NCH + cc];
+    A.w[i] = ld_stream16_buf(pr, (uint32_t)rr * (uint32_t)(F / 2) + (uint32_t)cc * 16u);
+    A.s[i] = ld_byte_buf(sr, (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc);
   }
 #pragma unroll
   for (int b = 0; b < kDnK; ++b)
