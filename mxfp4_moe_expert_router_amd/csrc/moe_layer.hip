@@ -678,7 +678,12 @@ __device__ __forceinline__ int row_at(const int* cum, int na, int R, int w, int 
   // far above the rounding error, so the floors are exact.
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t X = (int64_t)uni(cum[na]) * w;
-  const int cq = (int)floor((double)X / (double)G);  // floor(c / R)
+  // G is a power of two in the launches the library makes (a grid of one
+  // workgroup per CU, times the rounds): then the floors are shifts
+  const bool pow2 = (G & (G - 1)) == 0;
+  const int sh = __builtin_ctz((unsigned)G);
+  const auto fdiv = [&](int64_t v) { return pow2 ? (int)(v >> sh) : (int)floor((double)v / (double)G); };
+  const int cq = fdiv(X);  // floor(c / R)
   const uint64_t b1 = __ballot(cum[min(lane * 16, na)] <= cq);  // a prefix of the lanes, lane 0 set
   const int L = 63 - __clzll(b1);
   const int i2 = min(L * 16 + lane, na);
@@ -689,7 +694,7 @@ __device__ __forceinline__ int row_at(const int* cum, int na, int R, int w, int 
   const int u = uni(cum[lo + 1]) - c0;
   // c - R * cum[lo] = floor(R * (X - G * cum[lo]) / G), with 0 <= X - G * cum[lo] < G * u
   const int64_t t = (int64_t)R * (X - (int64_t)G * c0);
-  const int rem = (int)floor((double)t / (double)G);
+  const int rem = fdiv(t);
   const int i = (rem + u - 1) / u;
   return lo * R + min(i, R);
 }
@@ -1446,7 +1451,6 @@ __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, u
   return down_loop<false>(P, S, tag, hb0);
 }
 
-
 template <int MM, bool HS>
 __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int wg, int G,
                                               size_t x_bytes) {
@@ -1498,19 +1502,22 @@ __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int w
     __syncthreads();
     return;
   }
-  // waves 0-3: the gate/up chunk boundaries, b = 2k + side of chunk k (side 0
-  // its start, 1 its end); waves 4-7: the two down chunks' boundaries
-  if (wave < 4) {
+  // The gate/up chunk boundaries b = 2k + side of chunk k (side 0 its start,
+  // 1 its end), two per wave; waves 4 and 5 also the two down chunks'
+  // boundaries (the searches of one wave run one after another: four per
+  // wave on waves 0-3 took ~1 us more before the first weight loads)
+  {
     int* tab = round_tab(S, 0);
     const int nr = P.xmode ? 1 : kRounds;  // xmode 1: one range (its pairs' x is staged)
-    for (int b = wave; b < 2 * nr; b += 4) {
+    for (int b = wave; b < 2 * nr; b += kWaves) {
       const int k = b >> 1, side = b & 1;
       const int v = row_at(S.cgu, na, P.F, k * G + wg + side, nr * G);
       if (lane == 0) tab[side ? kRounds + k : k] = v;  // ends parked where the lengths go
     }
     if (wave == 0 && lane == 0)
       for (int c = nr; c < kRounds; ++c) tab[c] = tab[kRounds + c] = 0;  // empty chunks
-  } else if (wave < 6) {
+  }
+  if (wave == 4 || wave == 5) {
     int* tab = round_tab(S, 1);
     const int side = wave & 1;
     const int v = row_at(S.cdn, na, P.d / kDnRows, wg + side, G);
@@ -1521,16 +1528,20 @@ __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int w
     }
   }
   __syncthreads();
-  if (threadIdx.x < 2) {
-    int* t = round_tab(S, threadIdx.x);
-    int run = 0;
-    for (int k = 0; k < kRounds; ++k) {
-      const int len = t[kRounds + k] - t[k];
-      t[kRounds + k] = run;
-      run += len;
-    }
-    t[2 * kRounds] = run;
-    S.misc[1 + threadIdx.x] = 0;
+  // chunk lengths -> cumulative starts, both tables at once by wave 0: lanes
+  // 0-7 (gate/up) and 32-39 (down) hold a chunk's length; exclusive sums
+  // within each group of 32 lanes by the wave scan (the upper group's scan
+  // starts from the lower group's total, which is subtracted)
+  if (wave == 0) {
+    const int ph = lane >> 5, k = lane & 31;
+    int* t = round_tab(S, ph);
+    const int len = k < kRounds ? t[kRounds + k] - t[k] : 0;
+    const int inc = wave_inclusive_scan(len);
+    const int base = __shfl(inc, 31);  // the lower group's total
+    const int incl = ph ? inc - base : inc;
+    if (k < kRounds) t[kRounds + k] = incl - len;
+    if (k == kRounds - 1) t[2 * kRounds] = incl;
+    if (k == 0) S.misc[1 + ph] = 0;
   }
   __syncthreads();
 }
