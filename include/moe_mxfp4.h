@@ -229,7 +229,11 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
 
 /* Byte offsets of the intermediates inside a workspace after a forward call
  * (for inspection).  h = SwiGLU activations [T*topk][ffn] in pair order (the
- * order of sorted_slot) and y = gated expert outputs [T*topk][d] in slot order
+ * order of sorted_slot; within a pair's row the values are in order when
+ * h_chunk_major is 0, else value i = 32 c + e is word 2 ((e / 2) (ffn / 32) + c)
+ * + e % 2 of the row, the order the small-batch path with x of every token in
+ * LDS reads in its down step) and
+ * y = gated expert outputs [T*topk][d] in slot order
  * (row t*topk + j holds gate[t][j] * y(expert_j, t)) are 64-bit words whose low
  * 32 bits are the fp32 value (the high 32 bits are a tag); logits fp32 [T][E];
  * topk_idx int32 [T][topk]; topk_w fp32 [T][topk]; offsets int32 [E+1];
@@ -238,7 +242,8 @@ int moe_mxfp4_route(const moe_mxfp4_dims* dims, const void* x, const float* rout
  * [T][d], after a stack call (moe_mxfp4_forward_layers) the normalised input
  * of its last layer. */
 typedef struct {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, trace, x_last, total;
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, pos, active, n_active, h, y, trace, x_last, h_chunk_major,
+      total;
 } moe_mxfp4_ws_layout;
 int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxfp4_ws_layout* layout);
 

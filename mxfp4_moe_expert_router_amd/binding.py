@@ -45,7 +45,7 @@ class Options(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_idx", "topk_w", "offsets", "sorted_slot", "pos", "active", "n_active", "h", "y", "trace",
-                 "x_last", "total")]
+                 "x_last", "h_chunk_major", "total")]
 
 
 def _load():
@@ -319,6 +319,9 @@ def intermediates(workspace: torch.Tensor, dims: LayerDims, topk: int) -> dict:
         words = workspace[off: off + n * 8].view(torch.int32).view(n, 2)
         return words[:, 0].contiguous().view(torch.float32)
 
+    h = tagged(lay.h, TK * F).view(TK, F)
+    if lay.h_chunk_major:  # row order: value 32 c + e at word 2 ((e / 2) (F / 32) + c) + e % 2
+        h = h.view(TK, 16, F // 32, 2).permute(0, 2, 1, 3).reshape(TK, F)
     return {
         "logits": view(lay.logits, T * E, torch.float32).view(T, E),
         "topk_idx": view(lay.topk_idx, TK, torch.int32).view(T, topk),
@@ -328,7 +331,7 @@ def intermediates(workspace: torch.Tensor, dims: LayerDims, topk: int) -> dict:
         "pos": view(lay.pos, TK, torch.int32),
         "active": view(lay.active, E, torch.int32),
         "n_active": view(lay.n_active, 1, torch.int32),
-        "h": tagged(lay.h, TK * F).view(TK, F),
+        "h": h,
         "y": tagged(lay.y, TK * d).view(TK, d),
         "trace": view(lay.trace, 2048 * 16, torch.int64).view(2048, 16),
         "x_last": view(lay.x_last, T * d, torch.int16).view(T, d),

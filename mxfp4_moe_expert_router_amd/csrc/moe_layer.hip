@@ -959,6 +959,18 @@ __device__ __forceinline__ void gu_load(const Params& P, const Smem& S, int rho,
 
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
+// Order of a pair's F tagged h words on the small-batch path with x of every
+// token in LDS (xmode 0, chunk-major): value i (chunk c = i / 32, element
+// e = i % 32 of it) is word 2 ((e / 2) NCH + c) + e % 2, so 16-byte piece
+// v NCH + c holds values 32 c + 2 v and 32 c + 2 v + 1.  A wave whose lane c
+// needs chunk c (the down step) then reads NCH consecutive pieces per load
+// instruction (1 KiB at F = 2048) instead of one piece 256 bytes apart per
+// lane.  Measured on MI355X, 8 tokens: -1% per layer (gate/up +2 us for its
+// scattered 8-byte stores, down -4 us).  With more tokens (xmode 1, more h
+// stores per row) the stores cost more than the loads save (16 tokens: +3%),
+// so there, and on the MFMA path, h stays in value order ([pair][F]).
+__device__ __forceinline__ int h_word(int i, int nch) { return 2 * (((i & 31) >> 1) * nch + (i >> 5)) + (i & 1); }
+
 // Small batches: x in LDS (xmode 0: row t = token t; xmode 1: row r = pair
 // xbase + r, see stage_pairs).  Each chunk of the row pair is decoded once and
 // used for up to kGUTok tokens.  A token group whose pairs are not in LDS
@@ -1015,7 +1027,8 @@ __device__ __forceinline__ void gu_compute_resident(const Params& P, const Smem&
       if (t < nb) {
         const float gs = wave_sum(g[t]), us = wave_sum(u[t]);
         if (lane == 0)
-          st_tagged(&P.hq[(size_t)(p0 + tb + t) * P.F + i], __builtin_bit_cast(uint32_t, swiglu(gs, us)), tag);
+          st_tagged(&P.hq[(size_t)(p0 + tb + t) * P.F + (XP ? i : h_word(i, P.F / 32))],
+                    __builtin_bit_cast(uint32_t, swiglu(gs, us)), tag);
       }
     }
   };
@@ -1151,14 +1164,17 @@ __device__ __forceinline__ void dn_load(const Params& P, int e, int r0, int nr, 
   }
 }
 
-// h of pair p into registers (the lane's chunks); waits for its tags.
-template <int MM>
+// h of pair p into registers (the lane's chunks); waits for its tags.  CM:
+// chunk-major rows (h_word), else value order.
+template <int MM, bool CM>
 __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, float (&h)[MM][32]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int NCH = P.F / 32;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.hq + (size_t)p * P.F, (uint32_t)P.F * 8u);
   const uint32_t want = tag + P.withhold_h;
   const uint64_t t0 = wall_clock64();
+  // chunk c: 16 pieces NCH pieces apart (CM), else 256 contiguous bytes
+  const uint32_t cstride = CM ? 16u : 256u, vstride = CM ? (uint32_t)NCH * 16u : 16u;
   int round = 0;
   // The first attempt reads the whole h at once and through the L2 (it is
   // usually complete by then, and under full load every round trip costs
@@ -1170,10 +1186,11 @@ __device__ __forceinline__ bool dn_load_h(const Params& P, uint32_t tag, int p, 
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
       const int c = lane + kWave * m;
-      const uint32_t base = (uint32_t)min(c, NCH - 1) * 256u;  // 32 tagged words per chunk
+      const uint32_t base = (uint32_t)min(c, NCH - 1) * cstride;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const u32x4_t w = round == 0 ? ld_cached16(rs, base + v * 16u) : ld_coherent16(rs, base + v * 16u);
+        const uint32_t off = base + (uint32_t)v * vstride;  // values 32 c + 2 v, +1
+        const u32x4_t w = round == 0 ? ld_cached16(rs, off) : ld_coherent16(rs, off);
         ok &= (w.y == want) && (w.w == want);
         h[m][2 * v] = c < NCH ? u2f(w.x) : 0.f;
         h[m][2 * v + 1] = c < NCH ? u2f(w.z) : 0.f;
@@ -1232,14 +1249,14 @@ __device__ __forceinline__ void dn_compute(const Params& P, const Smem& S, uint3
 // Rows [r, rend) of expert e's W_down against the h of NT-or-fewer pairs
 // starting at pair p (ntok of them), ROWS rows per step with the next step's
 // rows in flight.
-template <int MM, int NT, int ROWS>
+template <int MM, int NT, int ROWS, bool CM>
 __device__ __forceinline__ bool down_rows(const Params& P, const Smem& S, uint32_t tag, int e, int p, int ntok, int r,
                                           int rend) {
   float h[NT][MM][32];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     if (tt < ntok) {
-      if (!dn_load_h<MM>(P, tag, p + tt, h[tt])) return false;
+      if (!dn_load_h<MM, CM>(P, tag, p + tt, h[tt])) return false;
     }
   }
   DnRows<MM, ROWS> A, B;
@@ -1257,7 +1274,7 @@ __device__ __forceinline__ bool down_rows(const Params& P, const Smem& S, uint32
 
 // F > 2048: each wave streams a contiguous range of the n_active*d rows of
 // W_down (equal shares of the modelled work), one token per pass.
-template <int MM>
+template <int MM, bool CM>
 __device__ __forceinline__ bool down_waves_static(const Params& P, const Smem& S, uint32_t tag, int gw, int NW) {
   const int d = P.d;
   int q0, q1;
@@ -1270,7 +1287,7 @@ __device__ __forceinline__ bool down_waves_static(const Params& P, const Smem& S
     const int p0 = uni(S.off[e]), ne = uni(S.off[e + 1]) - p0;
     const int r0 = rho - a * d, rend = seg_end - a * d;
     for (int tg = 0; tg < ne; ++tg)
-      if (!down_rows<MM, 1, 2>(P, S, tag, e, p0 + tg, 1, r0, rend)) return false;
+      if (!down_rows<MM, 1, 2, CM>(P, S, tag, e, p0 + tg, 1, r0, rend)) return false;
     rho = seg_end;
   }
   return true;
@@ -1290,7 +1307,7 @@ __device__ __forceinline__ void dn_unit_rows(const Params& P, const Smem& S, int
 // pass (kept in registers across units it costs more registers than the
 // wave has); else each wave loads the h it needs from global memory and keeps
 // it across the units of the same expert and token pair.
-template <bool HL>
+template <bool HL, bool CM>
 __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uint32_t tag, int u,
                                              const DnRows<1, kDnRows>& R, float (&h)[2][1][32], int& ha, int& hb,
                                              int hb0) {
@@ -1306,19 +1323,31 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
       // codes have scale byte 0 (dn_load), 2^-127, which puts their terms far
       // below the rounding of the sums (see gu_load)
       float hl[2][1][32];
-      const int c = min(lane, P.F / 32 - 1);
+      const int nch = P.F / 32, c = min(lane, nch - 1);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int pr = p0 + tg + min(tt, nt - 1);
-        const f32x4_t* hp =
-            reinterpret_cast<const f32x4_t*>(S.xs) + ((size_t)(pr - hb0) * P.F + (size_t)c * 32) / 4;
+        if (CM) {
+          // chunk-major rows (h_word): lane c reads values 32 c + 2 v, +1 at
+          // 8-byte word v NCH + c (consecutive lanes, consecutive words)
+          const f32x2_t* hp = reinterpret_cast<const f32x2_t*>(S.xs) + ((size_t)(pr - hb0) * P.F) / 2 + c;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const f32x4_t q = hp[v];
-          hl[tt][0][4 * v] = q.x;
-          hl[tt][0][4 * v + 1] = q.y;
-          hl[tt][0][4 * v + 2] = q.z;
-          hl[tt][0][4 * v + 3] = q.w;
+          for (int v = 0; v < 16; ++v) {
+            const f32x2_t q = hp[v * nch];
+            hl[tt][0][2 * v] = q.x;
+            hl[tt][0][2 * v + 1] = q.y;
+          }
+        } else {
+          const f32x4_t* hp =
+              reinterpret_cast<const f32x4_t*>(S.xs) + ((size_t)(pr - hb0) * P.F + (size_t)c * 32) / 4;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const f32x4_t q = hp[v];
+            hl[tt][0][4 * v] = q.x;
+            hl[tt][0][4 * v + 1] = q.y;
+            hl[tt][0][4 * v + 2] = q.z;
+            hl[tt][0][4 * v + 3] = q.w;
+          }
         }
       }
       dn_compute<1, 2, kDnRows>(P, S, tag, p0 + tg, nt, r, kDnRows, R, hl);
@@ -1327,7 +1356,7 @@ __device__ __forceinline__ bool dn_unit_work(const Params& P, const Smem& S, uin
     if (ha != a || hb != tg) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        if (tt < nt && !dn_load_h<1>(P, tag, p0 + tg + tt, h[tt])) return false;
+        if (tt < nt && !dn_load_h<1, CM>(P, tag, p0 + tg + tt, h[tt])) return false;
       if (ha < 0) stamp(P, blockIdx.x, 8);  // trace: the first h this wave needs is present
       ha = a;
       hb = tg;
@@ -1383,6 +1412,7 @@ __device__ __forceinline__ bool stage_h(const Params& P, const Smem& S, uint32_t
       // first read through the L2 (dropped of earlier calls' lines, see k_layer)
       const u32x4_t w = round == 0 ? ld_cached16(rs, (uint32_t)i * 16u) : ld_coherent16(rs, (uint32_t)i * 16u);
       if (w.y == tag + P.withhold_h && w.w == tag + P.withhold_h) {
+        // the rows keep the order of the tagged words (h_word for xmode 0)
         hl[2 * i] = u2f(w.x);
         hl[2 * i + 1] = u2f(w.z);
       } else {
@@ -1408,7 +1438,7 @@ __device__ __forceinline__ bool stage_h(const Params& P, const Smem& S, uint32_t
 // and load the next unit's rows while computing the current one.  An
 // expert's tokens are taken two at a time, so W_down is read once per two
 // tokens.  HL: h from LDS (stage_h).
-template <bool HL>
+template <bool HL, bool CM>
 __device__ __forceinline__ bool down_loop(const Params& P, const Smem& S, uint32_t tag, int hb0) {
   const int* tab = round_tab(S, 1);
   const int U1 = uni(tab[2 * kRounds]);
@@ -1426,12 +1456,12 @@ __device__ __forceinline__ bool down_loop(const Params& P, const Smem& S, uint32
     const int u1 = j1 < U1 ? unit_of(tab, cur, j1) : u0;  // past the end: re-read (cache-hot), unused
     dn_unit_rows(P, S, u1, B);
     const int j2 = grab(ctr);
-    if (!dn_unit_work<HL>(P, S, tag, u0, A, h, ha, hb, hb0)) return false;
+    if (!dn_unit_work<HL, CM>(P, S, tag, u0, A, h, ha, hb, hb0)) return false;
     if (j1 >= U1) break;
     const int u2 = j2 < U1 ? unit_of(tab, cur, j2) : u1;
     dn_unit_rows(P, S, u2, A);
     const int j3 = grab(ctr);
-    if (!dn_unit_work<HL>(P, S, tag, u1, B, h, ha, hb, hb0)) return false;
+    if (!dn_unit_work<HL, CM>(P, S, tag, u1, B, h, ha, hb, hb0)) return false;
     if (j2 >= U1) break;
     u0 = u2;
     j1 = j3;
@@ -1440,22 +1470,23 @@ __device__ __forceinline__ bool down_loop(const Params& P, const Smem& S, uint32
 }
 
 // HS: the workgroup may stage h in LDS (stage_h; all threads, x_bytes = the x
-// area it may use); else every wave loads its own h.
-template <bool HS>
+// area it may use); else every wave loads its own h.  CM: h rows in the
+// chunk-major order of h_word (x of every token in LDS), else value order.
+template <bool HS, bool CM>
 __device__ __forceinline__ bool down_waves_dyn(const Params& P, const Smem& S, uint32_t tag, size_t x_bytes) {
-  if (!HS) return down_loop<false>(P, S, tag, 0);
+  if (!HS) return down_loop<false, CM>(P, S, tag, 0);
   bool staged;
   int hb0;
   if (!stage_h(P, S, tag, x_bytes, staged, hb0)) return false;
-  if (staged) return down_loop<true>(P, S, tag, hb0);  // uniform
-  return down_loop<false>(P, S, tag, hb0);
+  if (staged) return down_loop<true, CM>(P, S, tag, hb0);  // uniform
+  return down_loop<false, CM>(P, S, tag, hb0);
 }
 
-template <int MM, bool HS>
+template <int MM, bool HS, bool CM>
 __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, uint32_t tag, int wg, int G,
                                               size_t x_bytes) {
-  if (MM == 1) return down_waves_dyn<HS>(P, S, tag, x_bytes);
-  return down_waves_static<MM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
+  if (MM == 1) return down_waves_dyn<HS, CM>(P, S, tag, x_bytes);
+  return down_waves_static<MM, CM>(P, S, tag, wg * kWaves + uni(threadIdx.x / kWave), G * kWaves);
 }
 
 // The workgroup's share of the expert steps.  Work units: small-batch path,
@@ -2335,7 +2366,7 @@ __global__ void __launch_bounds__(kWG) k_layer(Params P) {
       gate_up_waves<XP>(P, S, tag, wg, G);
       stamp(P, wg, 4);
       stamp_gu_wave(P, wg);
-      dn = down_dispatch<MM, HS>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
+      dn = down_dispatch<MM, HS, !XP>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
     } else {
       gate_up_mfma(P, S, tag, wg, G);
       stamp(P, wg, 4);
@@ -2566,7 +2597,7 @@ __global__ void __launch_bounds__(kWG) k_stack(Params P0) {
       set_ranges(P, S, wg, G);
       if (wg < 8 && threadIdx.x >= kWG - kWave) invalidate_l2();
       gate_up_waves<false>(P, S, tag, wg, G);
-      bool dn = down_dispatch<MM, HS>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
+      bool dn = down_dispatch<MM, HS, true>(P, S, tag, wg, G, (size_t)P.xrows * P.d * 2);
       if (dn) dn = combine_step(P, tag, gw, NW, sl);
       if (!dn) s_ok = 0;
       // this wave's write-through stores of r have completed before the arrival
@@ -2662,7 +2693,10 @@ __global__ void __launch_bounds__(kWG) k_st_down(Params P) {
   } else {
     // the x area of this layout: the MFMA tiles or the masks, whichever is larger
     const LdsPlan L = lds_plan(P.T, P.d, P.E, P.k, 0);
-    down_dispatch<MM == 0 ? 1 : MM, true>(P, S, tag, blockIdx.x, gridDim.x, L.tki - L.xs);
+    if (P.xmode == 0)
+      down_dispatch<MM == 0 ? 1 : MM, true, true>(P, S, tag, blockIdx.x, gridDim.x, L.tki - L.xs);
+    else
+      down_dispatch<MM == 0 ? 1 : MM, true, false>(P, S, tag, blockIdx.x, gridDim.x, L.tki - L.xs);
   }
 }
 __global__ void __launch_bounds__(kWG) k_st_combine(Params P) {
@@ -3040,6 +3074,8 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_dims* dims, int32_t topk, moe_mxf
   out->y = L.yq;
   out->trace = L.trace;
   out->x_last = L.xb;
+  Launch Lp;
+  out->h_chunk_major = plan_launch(dims, topk, &Lp) == MOE_OK && Lp.small && Lp.xmode == 0 ? 1 : 0;
   out->total = L.total;
   return MOE_OK;
 }
