@@ -163,6 +163,35 @@ def test_all_tokens_same_experts(env):
     assert (np.diff(ref.offsets)[:3] == cfg.T).all()
 
 
+@pytest.mark.parametrize("E,k,tied,label", [
+    (16, 4, [2, 5, 9, 12], "four_tied_on_top"),   # the whole top-k is one tie
+    (16, 3, [1, 4, 6, 10, 14], "tie_straddles_k"),  # five equal logits, three taken
+    (300, 5, [7, 33, 140, 141, 299], "wide_E_tie"),  # more than 256 experts
+    (16, 4, None, "all_zero_router"),             # every logit +0: experts 0..k-1
+])
+def test_tied_logits(env, E, k, tied, label):
+    """Equal logits are ordered by expert index (lower first): router rows
+    that are exact copies give bit-equal logits on both sides."""
+    torch, moe, oracle, synth = env
+    cfg = synth.Config(label, T=5, d=256, F=64, E=E, k=k)
+    x, wr, p, s = inputs_for(synth, cfg)
+    wr = wr.copy()
+    if tied is None:
+        wr[:] = 0.0
+    else:
+        xf = synth.bf16_to_f32(x).copy()
+        xf[:, 0] = 1.0
+        x = synth.f32_to_bf16(xf)
+        row = wr[tied[0]].copy()
+        row[0] = 40.0  # far above the other logits
+        wr[tied] = row
+    got, ref, it = run_case(env, cfg, x=x, wr=wr, p=p, s=s, label=label)
+    if tied is None:
+        assert (ref.idx == np.arange(k)).all()
+    else:
+        assert (ref.idx[:, :min(k, len(tied))] == np.array(tied[:k])).all()
+
+
 def test_single_expert_layer(env):
     cfg = env[3].Config("one", T=4, d=320, F=64, E=1, k=1)
     run_case(env, cfg)
