@@ -15,6 +15,7 @@ namespace moe {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -361,6 +362,10 @@ __device__ __forceinline__ u32x4_t ld_stream16_buf(__amdgpu_buffer_rsrc_t r, uin
 }
 __device__ __forceinline__ uint32_t ld_byte_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, byte_off, 0, 0);
+}
+// 8-byte streaming load through a buffer descriptor (byte_off a multiple of 8).
+__device__ __forceinline__ u32x2_t ld_stream8_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 2);
 }
 
 // Drops this XCD's L2 lines (and the CU's vector cache), so that later cached

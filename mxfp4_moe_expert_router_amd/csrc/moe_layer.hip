@@ -1653,7 +1653,8 @@ __device__ __forceinline__ int seg_count(const Smem& S, int U0, int U1, int R, i
 // ---- gate/up ----
 struct GUA {
   u32x4_t g[kGUK], u[kGUK];
-  uint32_t sg[kGUK], su[kGUK];  // scale bytes as loaded
+  uint32_t sg[kGUK], su[kGUK];  // scale bytes as loaded (byte loads)
+  u32x4_t sv;                   // wide scale loads: lane l < 16 row l of W_gate, 16 <= l < 32 row l - 16 of W_up
   uint32_t keep;                // bit b: K block b's chunk is in range
 };
 
@@ -1668,7 +1669,12 @@ struct GUA {
 // moves the data into the MFMA layout when it is used.  Rows past F (last
 // unit of an expert) and chunks past d read a valid chunk and get a zero scale
 // at use.  Nothing is computed from the loaded data here, so the loads stay in
-// flight.
+// flight.  WS (d a multiple of 512, so a row's 16 scale bytes of a step are
+// 16-byte aligned): the scales of the step come in one 16-byte load per row
+// (lanes 0-15 W_gate, 16-31 W_up) instead of one byte load per lane per K
+// block and matrix, 1 load instruction instead of 8 (the loads' address
+// processing is one of the step's limits, see gu_mfma_take).
+template <bool WS>
 __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int R, GUA& A) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = d / 32;
@@ -1688,11 +1694,19 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
     const uint32_t so = (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc;
     A.g[i] = ld_stream16_buf(pr, po);
     A.u[i] = ld_stream16_buf(pr, po + up);
-    A.sg[i] = ld_byte_buf(sr, so);
-    A.su[i] = ld_byte_buf(sr, so + sup);
+    if (!WS) {
+      A.sg[i] = ld_byte_buf(sr, so);
+      A.su[i] = ld_byte_buf(sr, so + sup);
+    }
     // in range, for the MFMA-layout chunk this lane will hold for block i
     const int row = r0 + (lane & 15), ch = 16 * c.j + 4 * i + (lane >> 4);
     A.keep |= (row < F && ch < NCH) ? 1u << i : 0u;
+  }
+  if (WS) {
+    // bytes past the row's chunks (last step) belong to other rows or read
+    // past the descriptor (zeros); their chunks are out of range (keep)
+    const uint32_t so = (uint32_t)min(r0 + (lane & 15), F - 1) * (uint32_t)NCH + 16u * (uint32_t)c.j;
+    A.sv = ld_stream16_buf(sr, lane < 32 ? so + (lane >= 16 ? sup : 0u) : 0xFFFFFFF0u);
   }
 }
 // K block b of the MFMA layout from the loads: lane l = 16 h + r takes chunk
@@ -1707,6 +1721,7 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
 __device__ __forceinline__ uint32_t bperm(uint32_t v, int addr) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
 }
+template <bool WS>
 __device__ __forceinline__ void gu_mfma_take(const GUA& A, int b, u32x4_t& g, u32x4_t& u, uint32_t& sg,
                                              uint32_t& su) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1726,8 +1741,16 @@ __device__ __forceinline__ void gu_mfma_take(const GUA& A, int b, u32x4_t& g, u3
   u.y = pick(A.u[i0].y, A.u[i1].y);
   u.z = pick(A.u[i0].z, A.u[i1].z);
   u.w = pick(A.u[i0].w, A.u[i1].w);
-  sg = pick(A.sg[i0], A.sg[i1]);
-  su = pick(A.su[i0], A.su[i1]);
+  if (WS) {
+    // chunk 16 j + 4 b + h of row r: byte h of dword b of lane r (W_gate) or
+    // lane 16 + r (W_up)
+    const uint32_t d = b == 0 ? A.sv.x : b == 1 ? A.sv.y : b == 2 ? A.sv.z : A.sv.w;
+    sg = (bperm(d, 4 * r) >> (8 * h)) & 0xFFu;
+    su = (bperm(d, 4 * (16 + r)) >> (8 * h)) & 0xFFu;
+  } else {
+    sg = pick(A.sg[i0], A.sg[i1]);
+    su = pick(A.su[i0], A.su[i1]);
+  }
 }
 
 // x tile of step c: token rows n < 32 of the pass, K blocks kGUK j .. +kGUK,
@@ -1782,7 +1805,7 @@ __device__ __forceinline__ void gu_mfma_xstore(char* tile, const u32x4_t (&v)[kX
 
 // MFMAs of one step for this wave's tile against the x tile in LDS, for the
 // first NG column groups of 16 tokens.
-template <int NG>
+template <int NG, bool WS>
 __device__ __forceinline__ void gu_mfma_step(const GUA& A, const char* tile, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
   const int lane = threadIdx.x & (kWave - 1);
   const char* b0 = tile + (lane & 15) * kTileRow + (lane >> 4) * 64;
@@ -1797,7 +1820,7 @@ __device__ __forceinline__ void gu_mfma_step(const GUA& A, const char* tile, f32
     const bool in = (A.keep >> b) & 1u;
     u32x4_t cg, cu;
     uint32_t sgb, sub;
-    gu_mfma_take(A, b, cg, cu, sgb, sub);
+    gu_mfma_take<WS>(A, b, cg, cu, sgb, sub);
     bf16x8_t wg[4], wu[4];
     decode_chunk_a(cg, e8m0_to_f32(in ? sgb : 0u), wg);
     decode_chunk_a(cu, e8m0_to_f32(in ? sub : 0u), wu);
@@ -1845,17 +1868,18 @@ __device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int
 // in flight for two steps: with one step, a step's loads were waited for at
 // the next step (a step's compute and the x tile take less than one loaded
 // memory latency).
+template <bool WS>
 __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
                                             int q, int npos, Seg& cc, Seg& n1, Seg& n2, XRows& xrows, const GUA& Ac,
                                             GUA& An2, char* cur, char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
   u32x4_t xv[kXPieces];
   uint32_t xok;
   gu_mfma_xload(P, S, n1, xrows, xv, xok);  // first: waiting for it below must not wait for An2
-  gu_mfma_load(P, n2, R, An2);
+  gu_mfma_load<WS>(P, n2, R, An2);
   if (cc.ne - cc.pass > 16)
-    gu_mfma_step<2>(Ac, cur, ag, au);
+    gu_mfma_step<2, WS>(Ac, cur, ag, au);
   else
-    gu_mfma_step<1>(Ac, cur, ag, au);
+    gu_mfma_step<1, WS>(Ac, cur, ag, au);
   if (cc.j == nst - 1) gu_mfma_store(P, cc, R, tag, ag, au);
   if (q + 1 < npos) gu_mfma_xstore(nxt, xv, xok);
   seg_next(S, U1, R, nst, kGUPass, cc);
@@ -1867,7 +1891,8 @@ __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint
 // Gate/up + SwiGLU for the workgroup's units [U0, U1) (equal shares of the
 // modelled work).  All threads of the workgroup.  Three weight buffers
 // (steps q, q + 1, q + 2), two LDS x tiles.
-__device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+template <bool WS>
+__device__ __forceinline__ void gate_up_mfma_ws(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int R = (P.F + kGUUnitRows - 1) / kGUUnitRows;
   const int nst = (P.d + kGUK * kKB - 1) / (kGUK * kKB);
   const int U0 = uni(S.misc[5]), U1 = uni(S.misc[3]);
@@ -1891,8 +1916,8 @@ __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uin
     u32x4_t xv[kXPieces];
     uint32_t xok;
     gu_mfma_xload(P, S, cc, xrows, xv, xok);
-    gu_mfma_load(P, cc, R, A0);
-    gu_mfma_load(P, n1, R, A1);
+    gu_mfma_load<WS>(P, cc, R, A0);
+    gu_mfma_load<WS>(P, n1, R, A1);
     gu_mfma_xstore(cur, xv, xok);
     lds_barrier();
   }
@@ -1902,21 +1927,28 @@ __device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uin
     nxt = t;
   };
   for (int q = 0; q < npos; q += 3) {
-    gu_mfma_one(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, xrows, A0, A2, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, xrows, A0, A2, cur, nxt, ag, au);
     if (q + 1 >= npos) break;
     swap_tiles();
-    gu_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, xrows, A1, A0, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, xrows, A1, A0, cur, nxt, ag, au);
     if (q + 2 >= npos) break;
     swap_tiles();
-    gu_mfma_one(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, xrows, A2, A1, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, xrows, A2, A1, cur, nxt, ag, au);
     swap_tiles();
   }
+}
+__device__ __forceinline__ void gate_up_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  if (P.d % 512 == 0)  // uniform
+    gate_up_mfma_ws<true>(P, S, tag, wg, G);
+  else
+    gate_up_mfma_ws<false>(P, S, tag, wg, G);
 }
 
 // ---- down ----
 struct DnA {
   u32x4_t w[kDnK * kDnTiles];  // as loaded (load i)
-  uint32_t s[kDnK * kDnTiles]; // scale bytes as loaded
+  uint32_t s[kDnK * kDnTiles]; // scale bytes as loaded (byte loads)
+  u32x2_t sv;                  // wide scale loads: lane l the step's 8 scale bytes of row r0 + l
   uint32_t keep;               // bit b * kDnTiles + t: the MFMA-layout chunk of tile t, block b is in range
 };
 static_assert(kDnK == 2, "a step covers one 128-byte line (8 chunks) of each W_down row");
@@ -1925,7 +1957,10 @@ static_assert(kDnK == 2, "a step covers one 128-byte line (8 chunks) of each W_d
 // 64 * wave) of W_down, chunks 8 j .. 8 j + 7 (K = F): one 128-byte line per
 // row.  Load i takes rows r0 + 8 i + l / 8, chunk 8 j + l % 8 (whole lines; see
 // gu_mfma_load); dn_mfma_take moves tile t, block b into the MFMA layout
-// (lane l: row r0 + 16 t + l % 16, chunk 8 j + 4 b + l / 16).
+// (lane l: row r0 + 16 t + l % 16, chunk 8 j + 4 b + l / 16).  WS (ffn a
+// multiple of 256): the step's 8 scale bytes of row r0 + l in one 8-byte load
+// by lane l, 1 load instruction instead of 8 byte loads.
+template <bool WS>
 __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int R, DnA& A) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d = P.d, F = P.F, NCH = F / 32;
@@ -1941,8 +1976,9 @@ __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int 
   for (int i = 0; i < kDnK * kDnTiles; ++i) {
     const int rr = min(r0 + 8 * i + (lane >> 3), d - 1);
     A.w[i] = ld_stream16_buf(pr, (uint32_t)rr * (uint32_t)(F / 2) + (uint32_t)cc * 16u);
-    A.s[i] = ld_byte_buf(sr, (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc);
+    if (!WS) A.s[i] = ld_byte_buf(sr, (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc);
   }
+  if (WS) A.sv = ld_stream8_buf(sr, (uint32_t)min(r0 + lane, d - 1) * (uint32_t)NCH + 8u * (uint32_t)c.j);
 #pragma unroll
   for (int b = 0; b < kDnK; ++b)
 #pragma unroll
@@ -1953,6 +1989,7 @@ __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int 
 }
 // Tile t, block b in the MFMA layout: lane l = 16 h + r takes row 16 t + r,
 // chunk 4 b + h, held by load 2 t + (r >> 3) of lane 8 (r & 7) + 4 b + h.
+template <bool WS>
 __device__ __forceinline__ void dn_mfma_take(const DnA& A, int b, int t, u32x4_t& w, uint32_t& sc) {
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15, h = lane >> 4;
@@ -1967,7 +2004,10 @@ __device__ __forceinline__ void dn_mfma_take(const DnA& A, int b, int t, u32x4_t
   w.y = pick(A.w[i0].y, A.w[i1].y);
   w.z = pick(A.w[i0].z, A.w[i1].z);
   w.w = pick(A.w[i0].w, A.w[i1].w);
-  sc = pick(A.s[i0], A.s[i1]);
+  if (WS)  // chunk 8 j + 4 b + h of row 16 t + r: byte h of dword b of lane 16 t + r
+    sc = (bperm(b == 0 ? A.sv.x : A.sv.y, 4 * (16 * t + r)) >> (8 * h)) & 0xFFu;
+  else
+    sc = pick(A.s[i0], A.s[i1]);
 }
 
 // h tile of step c: pairs n < 32 of the pass, values 128(kDnK j) .. +128 kDnK
@@ -2046,7 +2086,7 @@ __device__ __forceinline__ bf16x8_t decode_op_a(const u32x4_t w, float scale, in
   return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-template <int NG>
+template <int NG, bool WS>
 __device__ __forceinline__ void dn_mfma_step(const DnA& A, const char* hi_tile, const char* lo_tile,
                                              f32x4_t (&acc)[kDnTiles][2]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -2058,7 +2098,7 @@ __device__ __forceinline__ void dn_mfma_step(const DnA& A, const char* hi_tile, 
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
       uint32_t sb;
-      dn_mfma_take(A, b, t, wt[t], sb);
+      dn_mfma_take<WS>(A, b, t, wt[t], sb);
       sc[t] = e8m0_to_f32((A.keep >> (b * kDnTiles + t)) & 1u ? sb : 0u);
     }
 #pragma unroll
@@ -2118,6 +2158,7 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
   }
 }
 
+template <bool WS>
 __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
                                             int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
                                             const DnA& Ac, DnA& An, char* cur, char* nxt,
@@ -2128,11 +2169,11 @@ __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint
   const bool ok = *bad == 0;
   u32x4_t hr[kHPieces];
   dn_mfma_hload<false>(P, nc, rs, hr);  // first: waiting for it below must not wait for An
-  dn_mfma_load(P, nc, R, An);
+  dn_mfma_load<WS>(P, nc, R, An);
   if (cc.ne - cc.pass > 16)
-    dn_mfma_step<2>(Ac, cur, cur + kHalf, acc);
+    dn_mfma_step<2, WS>(Ac, cur, cur + kHalf, acc);
   else
-    dn_mfma_step<1>(Ac, cur, cur + kHalf, acc);
+    dn_mfma_step<1, WS>(Ac, cur, cur + kHalf, acc);
   if (cc.j == nst - 1 && ok) dn_mfma_store(P, S, cc, R, tag, acc);
   if (q + 1 < npos) dn_mfma_hstore(P, nc, rs, tag, hr, nxt, nxt + kHalf, bad);
   seg_next(S, U1, R, nst, kDnPass, cc);
@@ -2142,7 +2183,8 @@ __device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint
 
 // Down projection for the workgroup's units [U0, U1).  All threads.  False
 // if an h wait was abandoned (then some of the units' results are not stored).
-__device__ __forceinline__ bool down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+template <bool WS>
+__device__ __forceinline__ bool down_mfma_ws(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   __shared__ int s_bad;
   const int R = (P.d + kDnUnitRows - 1) / kDnUnitRows;
   const int nst = (P.F + kDnK * kKB - 1) / (kDnK * kKB);
@@ -2165,17 +2207,22 @@ __device__ __forceinline__ bool down_mfma(const Params& P, const Smem& S, uint32
   {
     u32x4_t hr[kHPieces];
     dn_mfma_hload<false>(P, nc, rs, hr);
-    dn_mfma_load(P, nc, R, A0);
+    dn_mfma_load<WS>(P, nc, R, A0);
     dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf, &s_bad);
     seg_next(S, U1, R, nst, kDnPass, nc);
     lds_barrier();
   }
   for (int q = 0; q < npos; q += 2) {
-    dn_mfma_one(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc, &s_bad);
+    dn_mfma_one<WS>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc, &s_bad);
     if (q + 1 >= npos) break;
-    dn_mfma_one(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc, &s_bad);
+    dn_mfma_one<WS>(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc, &s_bad);
   }
   return s_bad == 0;  // after the last step's barrier: the same in every wave
+}
+__device__ __forceinline__ bool down_mfma(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
+  if (P.F % 256 == 0)  // uniform
+    return down_mfma_ws<true>(P, S, tag, wg, G);
+  return down_mfma_ws<false>(P, S, tag, wg, G);
 }
 
 // ---------------------------------------------------------- combine ---------
