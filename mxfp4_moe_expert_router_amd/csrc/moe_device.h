@@ -363,9 +363,9 @@ __device__ __forceinline__ u32x4_t ld_stream16_buf(__amdgpu_buffer_rsrc_t r, uin
 __device__ __forceinline__ uint32_t ld_byte_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, byte_off, 0, 0);
 }
-// 8-byte streaming load through a buffer descriptor (byte_off a multiple of 8).
-__device__ __forceinline__ u32x2_t ld_stream8_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 2);
+// 8-byte load through a buffer descriptor and the L2 (byte_off a multiple of 8).
+__device__ __forceinline__ u32x2_t ld_cached8_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
 }
 
 // Drops this XCD's L2 lines (and the CU's vector cache), so that later cached

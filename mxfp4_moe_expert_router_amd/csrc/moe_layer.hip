@@ -1704,9 +1704,12 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
   }
   if (WS) {
     // bytes past the row's chunks (last step) belong to other rows or read
-    // past the descriptor (zeros); their chunks are out of range (keep)
+    // past the descriptor (zeros); their chunks are out of range (keep).
+    // Through the L2 without the streaming hint: a 128-byte line of scales
+    // serves 8 steps of its row (streaming loads fetched it again for each:
+    // 1.3x the layer's HBM bytes at T=128 and T=512)
     const uint32_t so = (uint32_t)min(r0 + (lane & 15), F - 1) * (uint32_t)NCH + 16u * (uint32_t)c.j;
-    A.sv = ld_stream16_buf(sr, lane < 32 ? so + (lane >= 16 ? sup : 0u) : 0xFFFFFFF0u);
+    A.sv = ld_cached16(sr, lane < 32 ? so + (lane >= 16 ? sup : 0u) : 0xFFFFFFF0u);
   }
 }
 // K block b of the MFMA layout from the loads: lane l = 16 h + r takes chunk
@@ -1978,7 +1981,8 @@ __device__ __forceinline__ void dn_mfma_load(const Params& P, const Seg& c, int 
     A.w[i] = ld_stream16_buf(pr, (uint32_t)rr * (uint32_t)(F / 2) + (uint32_t)cc * 16u);
     if (!WS) A.s[i] = ld_byte_buf(sr, (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc);
   }
-  if (WS) A.sv = ld_stream8_buf(sr, (uint32_t)min(r0 + lane, d - 1) * (uint32_t)NCH + 8u * (uint32_t)c.j);
+  // (through the L2: a 128-byte line of scales serves 16 steps of its row)
+  if (WS) A.sv = ld_cached8_buf(sr, (uint32_t)min(r0 + lane, d - 1) * (uint32_t)NCH + 8u * (uint32_t)c.j);
 #pragma unroll
   for (int b = 0; b < kDnK; ++b)
 #pragma unroll
