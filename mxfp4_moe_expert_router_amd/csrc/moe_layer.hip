@@ -2019,12 +2019,18 @@ __device__ __forceinline__ void dn_mfma_take(const DnA& A, int b, int t, u32x4_t
 // kHRow, word pair = piece % kHRow).
 constexpr int kHRow = kDnK * kKB / 2;  // word pairs per pair row of a step
 constexpr int kHPieces = kDnPass * kHRow / kWG;
-template <bool COHERENT>
+// NR: the pass has at most NR pairs (16 or 32): only the pieces of its first
+// NR rows are loaded and written (a tile of at most 16 pairs feeds only the
+// first column group, so rows 16-31 are never read: 4 of the 8 loads per
+// thread per step saved, the loads' address processing being one of the
+// step's limits).
+template <bool COHERENT, int NR>
 __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
                                               u32x4_t (&v)[kHPieces]) {
+  static_assert(NR % (kWG / kHRow) == 0 && NR <= kDnPass, "whole pieces");
   const int np = min(kDnPass, c.ne - c.pass);
 #pragma unroll
-  for (int m = 0; m < kHPieces; ++m) {
+  for (int m = 0; m < NR / (kWG / kHRow); ++m) {
     const int pc = (int)threadIdx.x + kWG * m;
     const int n = pc / kHRow, k = c.j * kDnK * kKB + 2 * (pc % kHRow);
     // pieces past the pass's pairs or past F read past the descriptor's end:
@@ -2040,9 +2046,11 @@ __device__ __forceinline__ void dn_mfma_hload(const Params& P, const Seg& c, __a
 // the workgroup stores no more results), then writes it
 // as bf16 hi and lo tiles, layout [block][pair][272 bytes] each.  Values past
 // the pass or past F are zero.
+template <int NR>
 __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __amdgpu_buffer_rsrc_t rs,
                                                uint32_t tag, u32x4_t (&v)[kHPieces], char* hi_tile,
                                                char* lo_tile, int* bad) {
+  constexpr int kM = NR / (kWG / kHRow);  // pieces of the first NR rows
   const int np = min(kDnPass, c.ne - c.pass);
   auto used = [&](int m) {
     const int pc = (int)threadIdx.x + kWG * m;
@@ -2051,7 +2059,7 @@ __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __
   auto current = [&]() {
     bool ok = true;
 #pragma unroll
-    for (int m = 0; m < kHPieces; ++m) ok &= !used(m) || (v[m].y == tag + P.withhold_h && v[m].w == tag + P.withhold_h);
+    for (int m = 0; m < kM; ++m) ok &= !used(m) || (v[m].y == tag + P.withhold_h && v[m].w == tag + P.withhold_h);
     return ok;
   };
   if (!__all(current())) {
@@ -2064,12 +2072,12 @@ __device__ __forceinline__ void dn_mfma_hstore(const Params& P, const Seg& c, __
         *bad = 1;
         break;
       }
-      dn_mfma_hload<true>(P, c, rs, v);
+      dn_mfma_hload<true, NR>(P, c, rs, v);
       if (__all(current())) break;
     }
   }
 #pragma unroll
-  for (int m = 0; m < kHPieces; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int pc = (int)threadIdx.x + kWG * m;
     const int n = pc / kHRow, w = pc % kHRow;  // w: word pair within the step's values
     const int off = ((w >> 6) * kDnPass + n) * kTileRow + (w & 63) * 4;
@@ -2162,27 +2170,38 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
   }
 }
 
-template <bool WS>
-__device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
-                                            int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
-                                            const DnA& Ac, DnA& An, char* cur, char* nxt,
-                                            f32x4_t (&acc)[kDnTiles][2], int* bad) {
+template <bool WS, int NR>
+__device__ __forceinline__ void dn_mfma_one_nr(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+                                               int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
+                                               const DnA& Ac, DnA& An, char* cur, char* nxt,
+                                               f32x4_t (&acc)[kDnTiles][2], int* bad) {
   constexpr int kHalf = kDnK * kDnPass * kTileRow;  // hi tile; lo tile follows
   // read after the barrier that ended the previous step: set if any tile up to
   // the current one failed its wait (the flag never clears within a call)
   const bool ok = *bad == 0;
   u32x4_t hr[kHPieces];
-  dn_mfma_hload<false>(P, nc, rs, hr);  // first: waiting for it below must not wait for An
+  dn_mfma_hload<false, NR>(P, nc, rs, hr);  // first: waiting for it below must not wait for An
   dn_mfma_load<WS>(P, nc, R, An);
   if (cc.ne - cc.pass > 16)
     dn_mfma_step<2, WS>(Ac, cur, cur + kHalf, acc);
   else
     dn_mfma_step<1, WS>(Ac, cur, cur + kHalf, acc);
   if (cc.j == nst - 1 && ok) dn_mfma_store(P, S, cc, R, tag, acc);
-  if (q + 1 < npos) dn_mfma_hstore(P, nc, rs, tag, hr, nxt, nxt + kHalf, bad);
+  if (q + 1 < npos) dn_mfma_hstore<NR>(P, nc, rs, tag, hr, nxt, nxt + kHalf, bad);
   seg_next(S, U1, R, nst, kDnPass, cc);
   seg_next(S, U1, R, nst, kDnPass, nc);
   lds_barrier();
+}
+// The next tile (nc) decides which h pieces are loaded (dn_mfma_hload).
+template <bool WS>
+__device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+                                            int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
+                                            const DnA& Ac, DnA& An, char* cur, char* nxt,
+                                            f32x4_t (&acc)[kDnTiles][2], int* bad) {
+  if (nc.ne - nc.pass <= 16)  // uniform (an invalid nc loads nothing either way)
+    dn_mfma_one_nr<WS, 16>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
+  else
+    dn_mfma_one_nr<WS, kDnPass>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
 }
 
 // Down projection for the workgroup's units [U0, U1).  All threads.  False
@@ -2210,9 +2229,9 @@ __device__ __forceinline__ bool down_mfma_ws(const Params& P, const Smem& S, uin
   for (int t = 0; t < kDnTiles; ++t) acc[t][0] = acc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
     u32x4_t hr[kHPieces];
-    dn_mfma_hload<false>(P, nc, rs, hr);
+    dn_mfma_hload<false, kDnPass>(P, nc, rs, hr);
     dn_mfma_load<WS>(P, nc, R, A0);
-    dn_mfma_hstore(P, nc, rs, tag, hr, t0, t0 + kHalf, &s_bad);
+    dn_mfma_hstore<kDnPass>(P, nc, rs, tag, hr, t0, t0 + kHalf, &s_bad);
     seg_next(S, U1, R, nst, kDnPass, nc);
     lds_barrier();
   }
