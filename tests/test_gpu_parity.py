@@ -84,6 +84,7 @@ SMALL = [
     dict(T=100, d=2048, F=2080, E=16, k=4),    # MFMA path, F % 128 != 0
     dict(T=96, d=1024, F=256, E=4, k=2),       # MFMA path: ~48 tokens per expert, two token passes
     dict(T=100, d=800, F=96, E=3, k=2),        # MFMA path: partial K blocks and partial row units
+    dict(T=96, d=800, F=256, E=4, k=2),        # MFMA path: gate/up scales byte by byte, down scales 8 bytes a row
 ]
 
 
