@@ -50,8 +50,8 @@ class WsLayout(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build() or "
-                          f"python mxfp4_moe_expert_router_amd/build.py)")
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
+                          f"(run python mxfp4_moe_expert_router_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     P = ctypes.POINTER
