@@ -289,6 +289,57 @@ def test_withheld_h_leaves_nan_then_recovers(env, shape):
     assert rel_err(out.cpu().numpy(), ref.out) <= OUT_TOL
 
 
+ONE_TOKEN = [
+    dict(T=1, d=256, F=128, E=8, k=2),        # 4 chunks of ffn: slices of one chunk
+    dict(T=1, d=544, F=96, E=40, k=6),        # 3 chunks: three slices per expert, 17 chunks per d row
+    dict(T=1, d=800, F=2080, E=16, k=8),      # 65 chunks: 520 one-chunk slices, two per workgroup
+    dict(T=1, d=2048, F=1024, E=64, k=8),     # 32 chunks: one-chunk slices, 32 per expert
+    dict(T=1, d=512, F=4096, E=16, k=8),      # 128 chunks: four-chunk slices (16 rows per wave load)
+]
+
+
+@pytest.mark.parametrize("shape", ONE_TOKEN, ids=lambda s: "T{T}_d{d}_F{F}_E{E}_k{k}".format(**s))
+def test_one_token_kernel(env, shape):
+    """One-token layers (decode shapes): every output, h and y against the
+    oracle; the same bits with few workgroups (every unit still covered, each
+    sum in the same order) and launched cooperatively; the staged path within
+    the bar."""
+    torch, moe, oracle, synth = env
+    cfg = synth.Config("one_tok", **shape)
+    got, ref, it = run_case(env, cfg, label="one_token")
+    x, wr, p, s = inputs_for(synth, cfg)
+    xt, wrt, pt, st = to_device(torch, x, wr, p, s)
+    base = moe.forward(xt, wrt, pt, st, cfg.k)
+    for g in (1, 3, 37):
+        out = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(0, 0, g))
+        torch.cuda.synchronize()
+        assert torch.equal(out, base), g  # the sums do not depend on the split
+    coop = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(moe.MOE_OPT_COOPERATIVE, 0, 0))
+    staged = moe.forward(xt, wrt, pt, st, cfg.k, staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(coop, base)
+    assert rel_err(staged.cpu().numpy(), ref.out) <= OUT_TOL
+
+
+def test_one_token_watchdog(env):
+    # a one-token layer's top-k wait abandoned: all NaN, status TIMEOUT, then a
+    # normal call on the same workspace
+    torch, moe, oracle, synth = env
+    cfg = synth.Config("one_tok_hold", T=1, d=256, F=128, E=8, k=2)
+    x, wr, p, s = inputs_for(synth, cfg)
+    xt, wrt, pt, st = to_device(torch, x, wr, p, s)
+    dims = moe.LayerDims(cfg.T, cfg.d, cfg.F, cfg.E)
+    ws = moe.alloc_workspace(dims, cfg.k)
+    out = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws, options=moe.Options(moe.MOE_OPT_WITHHOLD_ARRIVAL, 2000, 0))
+    assert moe.status(ws) == moe.MOE_ETIMEOUT
+    assert torch.isnan(out).all()
+    moe.forward(xt, wrt, pt, st, cfg.k, out=out, workspace=ws)
+    assert moe.status(ws) == moe.MOE_OK
+    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
+    assert rel_err(out.cpu().numpy(), ref.out) <= OUT_TOL
+
+
 def test_small_grid_option(env):
     # a persistent launch with only a few workgroups still covers every unit
     torch, moe, oracle, synth = env
