@@ -650,20 +650,64 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 __device__ __forceinline__ int gu_cost(int n, int g) { return 16 + 5 * (n - 1) + 4 * ((n + g - 1) / g - 1); }
 __device__ __forceinline__ int dn_cost(int n, int F) { return F <= 2048 ? 14 * (n / 2) + 10 * (n % 2) : 10 * n; }
 
-// Work model of the MFMA path, per workgroup unit of an expert with n tokens:
-// weights stream at HBM speed until the MFMA work of a pass (its column
-// groups ng) exceeds it.
-__device__ __forceinline__ int gu_cost_mfma(int n) {
+// Work model of the MFMA path, per workgroup unit of an expert with n tokens,
+// in one scale for both steps (a workgroup's down units are dealt by its
+// gate/up work, see order_down): a
+// pass over a gate/up unit (128 rows each of W_gate and W_up, 128 d bytes of
+// codes) costs 7 d / 256 with one column group of 16 tokens and 8 d / 256
+// with two; a pass over a down unit (512 rows of W_down, 256 F bytes) costs
+// 16 F / 256 with one group and 22 F / 256 with two.  Fitted to per-workgroup
+// timings on MI355X at T=128 and T=512 (d=7168, ffn=2048): a gate/up unit
+// pass took 50 / 57 us, a down unit pass 31-36 / 43-45 us.
+__device__ __forceinline__ int gu_cost_mfma(int n, int d) {
+  const int s = (d + 255) / 256;
   int c = 0;
-  for (int p = 0; p < n; p += kGUPass) c += max(6, 2 * ((min(kGUPass, n - p) + 15) / 16));
+  for (int p = 0; p < n; p += kGUPass) c += s * (6 + (min(kGUPass, n - p) + 15) / 16);
   return c;
 }
-__device__ __forceinline__ int dn_cost_mfma(int n) {
+__device__ __forceinline__ int dn_cost_mfma(int n, int F) {
+  const int s = (F + 255) / 256;
   int c = 0;
-  for (int p = 0; p < n; p += kDnPass) c += max(10, 7 * ((min(kDnPass, n - p) + 15) / 16));
+  for (int p = 0; p < n; p += kDnPass) c += s * (10 + 6 * ((min(kDnPass, n - p) + 15) / 16));
   return c;
 }
 
+
+// MFMA path: the position of workgroup j among the XCD's per workgroups in
+// the order of their modelled gate/up work (least first, ties to the lower
+// index; workgroup i takes gate/up units S.misc[5] + i, + per, ... below
+// S.misc[3]).  The down units are dealt in turn in this order, so the
+// workgroups with less gate/up work take the down units left over after the
+// last full turn and start the turns first.  Dealt in turn by index instead,
+// the workgroups that ended the gate/up step last also took the extra down
+// units: at T=128 with Zipf routing the modelled shares explained the
+// per-workgroup times (correlation 0.96-0.97) and the layer ended ~100 us
+// after the median workgroup.  Wave 0; per <= 64.
+__device__ __forceinline__ int order_down(const Smem& S, int per, int j, int Rg) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int w = 0x7FFFFFFF;  // lanes past per: after every workgroup
+  {
+    const int g1 = uni(S.misc[3]);
+    int u = uni(S.misc[5]) + lane;
+    if (lane < per) {
+      w = 0;
+      if (u < g1) {
+        int a = u / Rg, rem = u - a * Rg;
+        while (u < g1) {
+          w += S.cgu[a + 1] - S.cgu[a];
+          u += per;
+          rem += per;
+          while (rem >= Rg) {
+            rem -= Rg;
+            ++a;
+          }
+        }
+      }
+    }
+  }
+  const int wj = __builtin_amdgcn_readlane(w, j);
+  return __popcll(__ballot(w < wj)) + __popcll(__ballot(w == wj) & ((1ull << j) - 1ull));
+}
 
 // Index, in the (active expert, row) list with R rows per expert, of the
 // first row whose modelled start lies at or after work position c (c in
@@ -751,8 +795,8 @@ __device__ __forceinline__ void build_perm_wave(const Params& P, const Smem& S, 
     }
     if (lane == 0) S.misc[0] = na;
     const int n = lane < na ? S.cgu[lane] : 0;
-    const int g = lane < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
-    const int dc = lane < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
+    const int g = lane < na ? (P.mfma ? gu_cost_mfma(n, P.d) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
+    const int dc = lane < na ? (P.mfma ? dn_cost_mfma(n, P.F) : dn_cost(n, P.F)) : 0;
     const int gi = wave_inclusive_scan(g), di = wave_inclusive_scan(dc);
     if (lane < na) {
       S.cgu[lane] = gi - g;
@@ -850,8 +894,8 @@ __device__ __forceinline__ void build_perm(const Params& P, const Smem& S, bool 
     for (int i = 0; i < 2; ++i) {
       const int a = e0 + i;
       const int n = a < na ? S.off[S.act[a] + 1] - S.off[S.act[a]] : 0;
-      g2[i] = a < na ? (P.mfma ? gu_cost_mfma(n) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
-      d2[i] = a < na ? (P.mfma ? dn_cost_mfma(n) : dn_cost(n, P.F)) : 0;
+      g2[i] = a < na ? (P.mfma ? gu_cost_mfma(n, P.d) : gu_cost(n, P.xmode ? kGUTok<true> : kGUTok<false>)) : 0;
+      d2[i] = a < na ? (P.mfma ? dn_cost_mfma(n, P.F) : dn_cost(n, P.F)) : 0;
       gs += g2[i];
       ds += d2[i];
     }
@@ -1500,9 +1544,12 @@ __device__ __forceinline__ bool down_dispatch(const Params& P, const Smem& S, ui
 //    workgroup, so a wave rarely needs a new h).  Work tables in round_tab;
 //    S.misc[1] / [2] = 0: gate/up and down counters over the workgroup's
 //    chunks.
-//  - MFMA path: per list, units U0, U0 + stride, ... below U1: S.misc[5] /
-//    [3] = gate/up U0 and U1 (S.misc[1] its counter), S.misc[6] / [4] = down
-//    U0 and U1 (S.misc[2]), S.misc[kMiscStride] = the stride (see below).
+//  - MFMA path: each list is cut into one chunk of equal modelled work per
+//    XCD (per workgroups), whose units are dealt in turn: gate/up units U0 +
+//    j, U0 + j + per, ... below U1 to workgroup j of the XCD, down units to
+//    the workgroups in the order of their modelled gate/up work (order_down).
+//    S.misc[5] / [3] = the workgroup's first gate/up unit and U1,
+//    S.misc[6] / [4] the same for down, S.misc[kMiscStride] = per.
 // All threads; ends with a barrier.
 __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int wg, int G) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -1518,18 +1565,22 @@ __device__ __forceinline__ void set_ranges(const Params& P, const Smem& S, int w
     // contiguous per-workgroup ranges: 32 experts' x per XCD, twice the L2).
     const int nx = (G % 8 == 0 && G >= 16) ? 8 : 1;
     const int per = G / nx, xcd = wg % nx, j = wg / nx;
+    const int Rg = (P.F + kGUUnitRows - 1) / kGUUnitRows;
     if (wave < 4) {  // waves 0-3: gate/up chunk start and end, down chunk start and end
       const bool gu = wave < 2;
-      const int R = gu ? (P.F + kGUUnitRows - 1) / kGUUnitRows : (P.d + kDnUnitRows - 1) / kDnUnitRows;
+      const int R = gu ? Rg : (P.d + kDnUnitRows - 1) / kDnUnitRows;
       const int v = row_at(gu ? S.cgu : S.cdn, na, R, xcd + (wave & 1), nx);
+      if (lane == 0) S.misc[wave == 0 ? 5 : wave == 1 ? 3 : wave == 2 ? 6 : 4] = v;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int pos = per <= kWave ? order_down(S, per, j, Rg) : j;
       if (lane == 0) {
-        if (wave == 0) S.misc[1] = S.misc[5] = v + j;
-        if (wave == 1) S.misc[3] = v;
-        if (wave == 2) S.misc[2] = S.misc[6] = v + j;
-        if (wave == 3) S.misc[4] = v;
+        S.misc[5] += j;
+        S.misc[6] += pos;
+        S.misc[kMiscStride] = per;
       }
     }
-    if (threadIdx.x == 0) S.misc[kMiscStride] = per;
     __syncthreads();
     return;
   }
@@ -1600,7 +1651,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Position in a workgroup's stream of (unit, token pass, K block).
 struct Seg {
-  int u, pass, j;   // unit index, first token of the pass, K block
+  int k, u, pass, j;  // index in the workgroup's list, unit, first token of the pass, K block
   int e, p0, ne;    // expert, its first pair, its tokens
   bool valid;
 };
@@ -1614,27 +1665,37 @@ __device__ __forceinline__ void seg_unit(const Smem& S, int u, int R, Seg& c) {
   c.ne = uni(S.off[c.e + 1]) - c.p0;
 }
 
-__device__ __forceinline__ void seg_start(const Smem& S, int U0, int U1, int R, Seg& c) {
-  c.valid = U0 < U1;
-  if (c.valid) seg_unit(S, U0, R, c);
+// Unit k of the workgroup's units of step ph (0 gate/up, 1 down), or -1 past
+// its end (see set_ranges).
+__device__ __forceinline__ int wg_unit(const Smem& S, int ph, int k) {
+  const int u = uni(S.misc[ph ? 6 : 5]) + k * uni(S.misc[kMiscStride]);
+  return u < uni(S.misc[ph ? 4 : 3]) ? u : -1;
 }
 
-__device__ __forceinline__ void seg_next(const Smem& S, int U1, int R, int nkb, int pass_len, Seg& c) {
+__device__ __forceinline__ void seg_start(const Smem& S, int ph, int R, Seg& c) {
+  c.k = 0;
+  const int u = wg_unit(S, ph, 0);
+  c.valid = u >= 0;
+  if (c.valid) seg_unit(S, u, R, c);
+}
+
+__device__ __forceinline__ void seg_next(const Smem& S, int ph, int R, int nkb, int pass_len, Seg& c) {
   if (!c.valid) return;
   if (++c.j < nkb) return;
   c.j = 0;
   c.pass += pass_len;
   if (c.pass < c.ne) return;
-  const int st = uni(S.misc[kMiscStride]);
-  if (c.u + st < U1) seg_unit(S, c.u + st, R, c);
+  const int u = wg_unit(S, ph, ++c.k);
+  if (u >= 0) seg_unit(S, u, R, c);
   else c.valid = false;
 }
 
-// Number of positions (unit, pass, K block) in units U0, U0 + stride, ... < U1.
-__device__ __forceinline__ int seg_count(const Smem& S, int U0, int U1, int R, int nkb, int pass_len) {
+// Number of positions (unit, pass, K block) in the workgroup's list of step ph.
+__device__ __forceinline__ int seg_count(const Smem& S, int ph, int R, int nkb, int pass_len) {
   int n = 0;
-  const int st = uni(S.misc[kMiscStride]);
-  for (int u = U0; u < U1; u += st) {
+  for (int k = 0;; ++k) {
+    const int u = wg_unit(S, ph, k);
+    if (u < 0) break;
     const int e = uni(S.act[u / R]);
     const int ne = uni(S.off[e + 1]) - uni(S.off[e]);
     n += (ne + pass_len - 1) / pass_len;
@@ -1661,8 +1722,9 @@ struct GUA {
 // This wave's tile of step c: rows r0 .. r0 + 15 (r0 = (u % R) * 128 + 16 *
 // wave) of W_gate and W_up, chunks 16 j .. 16 j + 15 (kGUK = 4 K blocks of 4
 // chunks).  The loads read whole 128-byte lines: load i takes rows
-// r0 + 8 (i & 1) + l / 8, chunks 16 j + 8 (i >> 1) + l % 8 (eight lanes per
-// row).  The MFMA layout wants lane l to hold row r0 + l % 16, chunk
+// r0 + 8 (i & 1) + (l / 4) % 8, chunks 16 j + 8 (i >> 1) + 4 (l / 32) + l % 4
+// (four lanes per 64-byte half of a row, lanes 0-31 the first halves).  The
+// MFMA layout wants lane l to hold row r0 + l % 16, chunk
 // 16 j + 4 b + l / 16 for K block b, i.e. four 64-byte pieces per row spread
 // over four loads; loads of that shape moved the same bytes in half-lines and
 // made the T=512 layer 25% slower (2.58 instead of 2.07 ms).  gu_mfma_take
@@ -1688,8 +1750,8 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
   A.keep = 0;
 #pragma unroll
   for (int i = 0; i < kGUK; ++i) {
-    const int rr = min(r0 + 8 * (i & 1) + (lane >> 3), F - 1);
-    const int cc = min(16 * c.j + 8 * (i >> 1) + (lane & 7), NCH - 1);
+    const int rr = min(r0 + 8 * (i & 1) + ((lane >> 2) & 7), F - 1);
+    const int cc = min(16 * c.j + 8 * (i >> 1) + 4 * (lane >> 5) + (lane & 3), NCH - 1);
     const uint32_t po = (uint32_t)rr * (uint32_t)(d / 2) + (uint32_t)cc * 16u;
     const uint32_t so = (uint32_t)rr * (uint32_t)NCH + (uint32_t)cc;
     A.g[i] = ld_stream16_buf(pr, po);
@@ -1714,13 +1776,13 @@ __device__ __forceinline__ void gu_mfma_load(const Params& P, const Seg& c, int 
 }
 // K block b of the MFMA layout from the loads: lane l = 16 h + r takes chunk
 // 4 b + h of row r, held by load 2 (b >> 1) + (r >> 3) of lane
-// 8 (r & 7) + 4 (b & 1) + h.  The permute's sources s and s + 32 share an LDS
-// bank (two-way conflicts: ~19% of the step's cycles stall on them), but the
-// load order that avoids them costs more: measured at T=512, loads with rows
-// varying fastest across the lanes made the gate/up step 11% slower and loads
-// with the chunks of a line rotated by the row 2% slower (the address
-// processing of the loads backs up when consecutive lanes do not read
-// consecutive bytes), the conflicts falling to 7% either way.
+// 32 (b & 1) + 4 (r & 7) + h: every permute reads one half of the wave.  With
+// eight lanes per whole line (sources 8 (r & 7) + 4 (b & 1) + h, in both
+// halves) the sources s and s + 32 shared an LDS bank, and the layer was ~1%
+// slower at T=128 and T=512.  Orders with rows varying fastest across the
+// lanes (11% slower gate/up step at T=512) or the chunks of a line rotated by
+// the row (2% slower) avoid the conflicts too but break the loads' runs of
+// consecutive bytes, which their address processing needs.
 __device__ __forceinline__ uint32_t bperm(uint32_t v, int addr) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
 }
@@ -1729,7 +1791,7 @@ __device__ __forceinline__ void gu_mfma_take(const GUA& A, int b, u32x4_t& g, u3
                                              uint32_t& su) {
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15, h = lane >> 4;
-  const int addr = 4 * (8 * (r & 7) + 4 * (b & 1) + h);
+  const int addr = 4 * (32 * (b & 1) + 4 * (r & 7) + h);
   const bool hi = r >= 8;
   const int i0 = 2 * (b >> 1), i1 = i0 + 1;
   const auto pick = [&](uint32_t a0, uint32_t a1) {
@@ -1872,7 +1934,7 @@ __device__ __forceinline__ void gu_mfma_store(const Params& P, const Seg& c, int
 // the next step (a step's compute and the x tile take less than one loaded
 // memory latency).
 template <bool WS>
-__device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+__device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint32_t tag, int R, int nst,
                                             int q, int npos, Seg& cc, Seg& n1, Seg& n2, XRows& xrows, const GUA& Ac,
                                             GUA& An2, char* cur, char* nxt, f32x4_t (&ag)[2], f32x4_t (&au)[2]) {
   u32x4_t xv[kXPieces];
@@ -1885,9 +1947,9 @@ __device__ __forceinline__ void gu_mfma_one(const Params& P, const Smem& S, uint
     gu_mfma_step<1, WS>(Ac, cur, ag, au);
   if (cc.j == nst - 1) gu_mfma_store(P, cc, R, tag, ag, au);
   if (q + 1 < npos) gu_mfma_xstore(nxt, xv, xok);
-  seg_next(S, U1, R, nst, kGUPass, cc);
-  seg_next(S, U1, R, nst, kGUPass, n1);
-  seg_next(S, U1, R, nst, kGUPass, n2);
+  seg_next(S, 0, R, nst, kGUPass, cc);
+  seg_next(S, 0, R, nst, kGUPass, n1);
+  seg_next(S, 0, R, nst, kGUPass, n2);
   lds_barrier();
 }
 
@@ -1898,17 +1960,16 @@ template <bool WS>
 __device__ __forceinline__ void gate_up_mfma_ws(const Params& P, const Smem& S, uint32_t tag, int wg, int G) {
   const int R = (P.F + kGUUnitRows - 1) / kGUUnitRows;
   const int nst = (P.d + kGUK * kKB - 1) / (kGUK * kKB);
-  const int U0 = uni(S.misc[5]), U1 = uni(S.misc[3]);
-  const int npos = seg_count(S, U0, U1, R, nst, kGUPass);
+  const int npos = seg_count(S, 0, R, nst, kGUPass);
   if (npos == 0) return;
   char* cur = reinterpret_cast<char*>(S.xs);
   char* nxt = cur + kGUK * kGUPass * kTileRow;
   Seg cc, n1, n2;
-  seg_start(S, U0, U1, R, cc);
+  seg_start(S, 0, R, cc);
   n1 = cc;
-  seg_next(S, U1, R, nst, kGUPass, n1);
+  seg_next(S, 0, R, nst, kGUPass, n1);
   n2 = n1;
-  seg_next(S, U1, R, nst, kGUPass, n2);
+  seg_next(S, 0, R, nst, kGUPass, n2);
   GUA A0, A1, A2;
   f32x4_t ag[2], au[2];
 #pragma unroll
@@ -1930,13 +1991,13 @@ __device__ __forceinline__ void gate_up_mfma_ws(const Params& P, const Smem& S, 
     nxt = t;
   };
   for (int q = 0; q < npos; q += 3) {
-    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q, npos, cc, n1, n2, xrows, A0, A2, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, R, nst, q, npos, cc, n1, n2, xrows, A0, A2, cur, nxt, ag, au);
     if (q + 1 >= npos) break;
     swap_tiles();
-    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q + 1, npos, cc, n1, n2, xrows, A1, A0, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, R, nst, q + 1, npos, cc, n1, n2, xrows, A1, A0, cur, nxt, ag, au);
     if (q + 2 >= npos) break;
     swap_tiles();
-    gu_mfma_one<WS>(P, S, tag, U1, R, nst, q + 2, npos, cc, n1, n2, xrows, A2, A1, cur, nxt, ag, au);
+    gu_mfma_one<WS>(P, S, tag, R, nst, q + 2, npos, cc, n1, n2, xrows, A2, A1, cur, nxt, ag, au);
     swap_tiles();
   }
 }
@@ -2171,7 +2232,7 @@ __device__ __forceinline__ void dn_mfma_store(const Params& P, const Smem& S, co
 }
 
 template <bool WS, int NR>
-__device__ __forceinline__ void dn_mfma_one_nr(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+__device__ __forceinline__ void dn_mfma_one_nr(const Params& P, const Smem& S, uint32_t tag, int R, int nst,
                                                int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
                                                const DnA& Ac, DnA& An, char* cur, char* nxt,
                                                f32x4_t (&acc)[kDnTiles][2], int* bad) {
@@ -2188,20 +2249,20 @@ __device__ __forceinline__ void dn_mfma_one_nr(const Params& P, const Smem& S, u
     dn_mfma_step<1, WS>(Ac, cur, cur + kHalf, acc);
   if (cc.j == nst - 1 && ok) dn_mfma_store(P, S, cc, R, tag, acc);
   if (q + 1 < npos) dn_mfma_hstore<NR>(P, nc, rs, tag, hr, nxt, nxt + kHalf, bad);
-  seg_next(S, U1, R, nst, kDnPass, cc);
-  seg_next(S, U1, R, nst, kDnPass, nc);
+  seg_next(S, 1, R, nst, kDnPass, cc);
+  seg_next(S, 1, R, nst, kDnPass, nc);
   lds_barrier();
 }
 // The next tile (nc) decides which h pieces are loaded (dn_mfma_hload).
 template <bool WS>
-__device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int U1, int R, int nst,
+__device__ __forceinline__ void dn_mfma_one(const Params& P, const Smem& S, uint32_t tag, int R, int nst,
                                             int q, int npos, __amdgpu_buffer_rsrc_t rs, Seg& cc, Seg& nc,
                                             const DnA& Ac, DnA& An, char* cur, char* nxt,
                                             f32x4_t (&acc)[kDnTiles][2], int* bad) {
   if (nc.ne - nc.pass <= 16)  // uniform (an invalid nc loads nothing either way)
-    dn_mfma_one_nr<WS, 16>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
+    dn_mfma_one_nr<WS, 16>(P, S, tag, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
   else
-    dn_mfma_one_nr<WS, kDnPass>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
+    dn_mfma_one_nr<WS, kDnPass>(P, S, tag, R, nst, q, npos, rs, cc, nc, Ac, An, cur, nxt, acc, bad);
 }
 
 // Down projection for the workgroup's units [U0, U1).  All threads.  False
@@ -2211,8 +2272,7 @@ __device__ __forceinline__ bool down_mfma_ws(const Params& P, const Smem& S, uin
   __shared__ int s_bad;
   const int R = (P.d + kDnUnitRows - 1) / kDnUnitRows;
   const int nst = (P.F + kDnK * kKB - 1) / (kDnK * kKB);
-  const int U0 = uni(S.misc[6]), U1 = uni(S.misc[4]);
-  const int npos = seg_count(S, U0, U1, R, nst, kDnPass);
+  const int npos = seg_count(S, 1, R, nst, kDnPass);
   if (npos == 0) return true;
   if (threadIdx.x == 0) s_bad = 0;
   lds_barrier();  // before any wave can set it
@@ -2221,7 +2281,7 @@ __device__ __forceinline__ bool down_mfma_ws(const Params& P, const Smem& S, uin
   char* t0 = reinterpret_cast<char*>(S.xs);
   char* t1 = t0 + 2 * kHalf;
   Seg cc, nc;
-  seg_start(S, U0, U1, R, cc);
+  seg_start(S, 1, R, cc);
   nc = cc;
   DnA A0, A1;
   f32x4_t acc[kDnTiles][2];
@@ -2232,13 +2292,13 @@ __device__ __forceinline__ bool down_mfma_ws(const Params& P, const Smem& S, uin
     dn_mfma_hload<false, kDnPass>(P, nc, rs, hr);
     dn_mfma_load<WS>(P, nc, R, A0);
     dn_mfma_hstore<kDnPass>(P, nc, rs, tag, hr, t0, t0 + kHalf, &s_bad);
-    seg_next(S, U1, R, nst, kDnPass, nc);
+    seg_next(S, 1, R, nst, kDnPass, nc);
     lds_barrier();
   }
   for (int q = 0; q < npos; q += 2) {
-    dn_mfma_one<WS>(P, S, tag, U1, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc, &s_bad);
+    dn_mfma_one<WS>(P, S, tag, R, nst, q, npos, rs, cc, nc, A0, A1, t0, t1, acc, &s_bad);
     if (q + 1 >= npos) break;
-    dn_mfma_one<WS>(P, S, tag, U1, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc, &s_bad);
+    dn_mfma_one<WS>(P, S, tag, R, nst, q + 1, npos, rs, cc, nc, A1, A0, t1, t0, acc, &s_bad);
   }
   return s_bad == 0;  // after the last step's barrier: the same in every wave
 }
