@@ -38,6 +38,20 @@ def kernel_hash() -> str:
     return m.hexdigest()[:16]
 
 
+def git_sha():
+    """The checked-out commit, or None where the tree carries no git metadata
+    (a copy of the sources; the source hashes of the line still identify the
+    kernel, the input generator and this script)."""
+    if not os.path.isdir(os.path.join(ROOT, ".git")):
+        return None
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return r.stdout.strip() or None if r.returncode == 0 else None
+
+
 def source_hash(rels) -> str:
     m = hashlib.sha256()
     for rel in rels:
@@ -306,6 +320,7 @@ def main():
         "kernel_hash": kernel_hash(),
         "generator_hash": source_hash(GENERATOR_SOURCES),
         "bench_hash": source_hash(["bench.py"]),
+        "git_sha": git_sha(),
         "preconditioning": pre,
         "host": host_info(),
         "stream_read_ref": dict(ref, layer_kernel_frac=round(kern_gbs / ref["GBs"], 4)),
@@ -482,6 +497,7 @@ def bench_stack(args):
             "kernel_us_mean": round(kern_s * 1e6, 2),
         },
         "kernel_hash": kernel_hash(),
+        "git_sha": git_sha(),
     }
     if not args.no_cpu_baseline:
         from oracle import oracle
