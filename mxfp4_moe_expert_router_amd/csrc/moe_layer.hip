@@ -111,7 +111,7 @@ struct Params {
   const uint8_t* scales;
   float* out;
   uint32_t* hdr;
-  uint64_t* lgp;   // [T][E rounded up to even] tagged logits
+  uint64_t* lgp;   // [T][E rounded up to even] tagged logits (two such arrays of partial sums, see router_halves)
   uint64_t* tk;    // [kTopkRep][T*k][2] tagged {expert id, gate} per slot, replicated
   uint64_t* hq;    // [T*k][F] tagged h, pair order
   uint64_t* yq;    // [T*k][d] tagged gate * y, slot order
@@ -331,77 +331,125 @@ __device__ __forceinline__ void stamp_gu_wave(const Params& P, int wg) {
 // (T=512: 58 us instead of 200).  A unit moves ~0.7 MB at one CU's share of
 // the bandwidth (~30 us), so for fewer tokens, with fewer units than CUs,
 // router_step's finer units finish first.  Unit =
-// (16 experts, 16 tokens), one workgroup; wave w sums K blocks of 16
-// [w nkb / 8, (w + 1) nkb / 8).  In K block j, lane l loads 4 consecutive K
+// (16 experts, 16 or 32 tokens, all or half of the K blocks), one workgroup
+// (router_token_blocks, router_halves); wave w sums the w-th eighth of the
+// unit's K blocks of 16.  In K block j, lane l loads 4 consecutive K
 // (16j + 4 (l / 16) .. +3) of expert row l % 16 and of token row l % 16, and
 // MFMA step s uses element s of both (each step sums a permuted but matching
 // set of 4 K).  The 8 partial tiles are added in wave order; a lane past the
 // last expert or token reads a clamped row and its result is not stored.
+// With router_halves = 2 a unit is one half of a tile's K blocks (units
+// u and u + tiles are the two halves of tile u), stored as partial logits in
+// the half's own array; the top-k adds the two in half order.
 // tile: kRouterTileBytes of LDS.
-__device__ __forceinline__ void router_mfma(const Params& P, uint32_t tag, int wg, int G, float* tile) {
+constexpr int kRouterSplitTiles = 128;  // router_mfma splits K up to this many 16 x 16 tiles
+__device__ __forceinline__ int router_halves(const Params& P) {
+  // At most 128 tiles (half a grid of one workgroup per CU): without the
+  // split half of the grid has no unit and the logits wait for the other half
+  // (T=128: ~30 us, one tile's 0.7 MB at one CU's share of the bandwidth).
+  // The choice depends on the shape only, so that the logits (and every
+  // result after them) are the same on any grid.
+  if (P.T <= kRouterMfmaT) return 1;
+  return ((P.E + 15) / 16) * ((P.T + 15) / 16) <= kRouterSplitTiles ? 2 : 1;
+}
+// TB = 2 where there are at least 512 16 x 16 tiles: a unit covers 32 tokens
+// (two 16-token blocks sharing each W_r load), so W_r is read T/32 instead of
+// T/16 times (T=512: 1.4 instead of 2.1 MB per workgroup, the step being
+// bound by these reads).  Shape only, as router_halves.
+__device__ __forceinline__ int router_token_blocks(const Params& P) {
+  if (P.T <= kRouterMfmaT) return 1;
+  return ((P.E + 15) / 16) * ((P.T + 15) / 16) >= 4 * kRouterSplitTiles ? 2 : 1;
+}
+// One unit: experts e0 .. e0 + 15, tokens t0 .. t0 + 16 TB - 1, K blocks
+// [kb0, kb1) of this wave; partial logits of half h.  All threads.
+template <int TB>
+__device__ __forceinline__ void router_unit(const Params& P, uint32_t tag, int e0, int t0, int h, int kb0, int kb1,
+                                            float* tile) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int ne16 = (P.E + 15) / 16, nt16 = (P.T + 15) / 16;
-  const int nkb = P.d / 16;
-  const int kb0 = wave * nkb / kWaves, kb1 = (wave + 1) * nkb / kWaves;
   const int E2 = (P.E + 1) & ~1;
   const int r = lane & 15, q = lane >> 4;
-  for (int u = wg; u < ne16 * nt16; u += G) {
-    const int e0 = (u / nt16) * 16, t0 = (u % nt16) * 16;
-    const f32x4_t* w = reinterpret_cast<const f32x4_t*>(P.wr + (size_t)min(e0 + r, P.E - 1) * P.d) + q;
-    const uint2* xr = reinterpret_cast<const uint2*>(P.x + (size_t)min(t0 + r, P.T - 1) * P.d) + q;
-    // K blocks in groups of kRB, the next group's loads in flight while the
-    // current one runs (blocks past kb1 re-read block kb1 - 1 and are skipped)
-    // four accumulators (one per MFMA step), so that consecutive MFMAs do not
-    // wait for each other's results; added at the end
-    constexpr int kRB = 8;
-    f32x4_t acc4[4];
+  const f32x4_t* w = reinterpret_cast<const f32x4_t*>(P.wr + (size_t)min(e0 + r, P.E - 1) * P.d) + q;
+  const uint2* xr[TB];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) acc4[s4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t a[2][kRB];
-    uint2 b[2][kRB];
-    const auto load = [&](int g, int j0) {
+  for (int bb = 0; bb < TB; ++bb)
+    xr[bb] = reinterpret_cast<const uint2*>(P.x + (size_t)min(t0 + 16 * bb + r, P.T - 1) * P.d) + q;
+  // K blocks in groups of kRB, the next group's loads in flight while the
+  // current one runs (blocks past kb1 re-read block kb1 - 1 and are skipped)
+  // four accumulators per token block (one per MFMA step), so that
+  // consecutive MFMAs do not wait for each other's results; added at the end
+  constexpr int kRB = 8;
+  f32x4_t acc4[TB][4];
 #pragma unroll
-      for (int i = 0; i < kRB; ++i) {
-        const int j = min(j0 + i, kb1 - 1);
-        a[g][i] = w[4 * j];
-        b[g][i] = xr[4 * j];
-      }
-    };
-    const auto run = [&](int g, int j0) {
+  for (int bb = 0; bb < TB; ++bb)
 #pragma unroll
-      for (int i = 0; i < kRB; ++i) {
-        if (j0 + i < kb1) {  // uniform
-          acc4[0] = mfma_f32(a[g][i].x, bf16lo(b[g][i].x), acc4[0]);
-          acc4[1] = mfma_f32(a[g][i].y, bf16hi(b[g][i].x), acc4[1]);
-          acc4[2] = mfma_f32(a[g][i].z, bf16lo(b[g][i].y), acc4[2]);
-          acc4[3] = mfma_f32(a[g][i].w, bf16hi(b[g][i].y), acc4[3]);
+    for (int s4 = 0; s4 < 4; ++s4) acc4[bb][s4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t a[2][kRB];
+  uint2 b[2][TB][kRB];
+  const auto load = [&](int g, int j0) {
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const int j = min(j0 + i, kb1 - 1);
+      a[g][i] = w[4 * j];
+#pragma unroll
+      for (int bb = 0; bb < TB; ++bb) b[g][bb][i] = xr[bb][4 * j];
+    }
+  };
+  const auto run = [&](int g, int j0) {
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      if (j0 + i < kb1) {  // uniform
+#pragma unroll
+        for (int bb = 0; bb < TB; ++bb) {
+          acc4[bb][0] = mfma_f32(a[g][i].x, bf16lo(b[g][bb][i].x), acc4[bb][0]);
+          acc4[bb][1] = mfma_f32(a[g][i].y, bf16hi(b[g][bb][i].x), acc4[bb][1]);
+          acc4[bb][2] = mfma_f32(a[g][i].z, bf16lo(b[g][bb][i].y), acc4[bb][2]);
+          acc4[bb][3] = mfma_f32(a[g][i].w, bf16hi(b[g][bb][i].y), acc4[bb][3]);
         }
       }
-    };
-    if (kb1 > kb0) {
-      load(0, kb0);
-      for (int j = kb0; j < kb1; j += 2 * kRB) {
-        load(1, j + kRB);
-        run(0, j);
-        if (j + kRB >= kb1) break;
-        load(0, j + 2 * kRB);
-        run(1, j + kRB);
-      }
     }
-    const f32x4_t acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  };
+  if (kb1 > kb0) {
+    load(0, kb0);
+    for (int j = kb0; j < kb1; j += 2 * kRB) {
+      load(1, j + kRB);
+      run(0, j);
+      if (j + kRB >= kb1) break;
+      load(0, j + 2 * kRB);
+      run(1, j + kRB);
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < TB; ++bb) {
+    const f32x4_t acc = (acc4[bb][0] + acc4[bb][1]) + (acc4[bb][2] + acc4[bb][3]);
     // D row = expert 4q + i, column = token r
 #pragma unroll
     for (int i = 0; i < 4; ++i) tile[wave * 256 + (4 * q + i) * 16 + r] = acc[i];
     __syncthreads();
     if (threadIdx.x < 256) {
-      const int ei = threadIdx.x >> 4, ti = threadIdx.x & 15;
+      const int ei = threadIdx.x >> 4, ti = threadIdx.x & 15, t = t0 + 16 * bb + ti;
       float l = 0.f;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) l += tile[v * 256 + ei * 16 + ti];
-      if (e0 + ei < P.E && t0 + ti < P.T)
-        st_tagged(&P.lgp[(size_t)(t0 + ti) * E2 + e0 + ei], __builtin_bit_cast(uint32_t, l), tag);
+      if (e0 + ei < P.E && t < P.T)
+        st_tagged(&P.lgp[((size_t)h * P.T + t) * E2 + e0 + ei], __builtin_bit_cast(uint32_t, l), tag);
     }
     __syncthreads();
+  }
+}
+__device__ __forceinline__ void router_mfma(const Params& P, uint32_t tag, int wg, int G, float* tile) {
+  const int wave = threadIdx.x / kWave;
+  const int tb = router_token_blocks(P), hs = router_halves(P);
+  const int ne16 = (P.E + 15) / 16, ntb = ((P.T + 15) / 16 + tb - 1) / tb, tiles = ne16 * ntb;
+  const int nkb = P.d / 16;
+  for (int u = wg; u < tiles * hs; u += G) {
+    const int tu = u % tiles, h = u / tiles;
+    const int e0 = (tu / ntb) * 16, t0 = (tu % ntb) * 16 * tb;
+    const int hb0 = h * nkb / hs, hn = (h + 1) * nkb / hs - hb0;
+    const int kb0 = hb0 + wave * hn / kWaves, kb1 = hb0 + (wave + 1) * hn / kWaves;
+    if (tb == 2)  // uniform
+      router_unit<2>(P, tag, e0, t0, h, kb0, kb1, tile);
+    else
+      router_unit<1>(P, tag, e0, t0, h, kb0, kb1, tile);
   }
 }
 
@@ -476,12 +524,15 @@ __device__ __forceinline__ void router_step(const Params& P, const Smem& S, uint
 // experts 2(L + 64m) + b in v[2m + b] (one 16-byte load per pair).
 // VPL: logits per lane (E <= 64 * VPL).
 template <int VPL>
-__device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t, int* out_i, float* out_w, bool debug) {
+__device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t, int hs, int* out_i, float* out_w,
+                                           bool debug) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t want = tag + P.withhold;
   const int E2 = (P.E + 1) & ~1, np = E2 / 2;
   float v[VPL];
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.lgp + (size_t)t * E2, (uint32_t)E2 * 8u);
+  // the second half's partial logits (router_halves = 2), else unused
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(P.lgp + ((size_t)(hs - 1) * P.T + t) * E2, (uint32_t)E2 * 8u);
   const uint64_t t0 = wall_clock64();
   int round = 0;
   for (;;) {
@@ -499,6 +550,17 @@ __device__ __forceinline__ bool topk_token(const Params& P, uint32_t tag, int t,
         if (2 * p + 1 < P.E) {
           ok &= q.w == want;
           v[2 * m + 1] = u2f(q.z);
+        }
+        if (hs == 2) {  // uniform: logit = first half + second half
+          const u32x4_t q2 = ld_coherent16(rs2, (uint32_t)min(p, np - 1) * 16u);
+          if (2 * p < P.E) {
+            ok &= q2.y == want;
+            v[2 * m] = v[2 * m] + u2f(q2.x);
+          }
+          if (2 * p + 1 < P.E) {
+            ok &= q2.w == want;
+            v[2 * m + 1] = v[2 * m + 1] + u2f(q2.z);
+          }
         }
       }
     }
@@ -568,11 +630,12 @@ __device__ __forceinline__ bool topk_publish(const Params& P, uint32_t tag, int 
   const int T = P.T, TK = P.T * P.k;
   int t = T <= NW ? (int)(((int64_t)gw * T + NW - 1) / NW) : gw;
   if (T <= NW && (t >= T || (int)((int64_t)t * NW / T) != gw)) return true;
+  const int hs = router_halves(P);
   for (; t < T; t += NW) {
     int ii;
     float ww;
-    const bool ok = P.E <= 4 * kWave ? topk_token<4>(P, tag, t, &ii, &ww, true)
-                                     : topk_token<kMaxE / kWave>(P, tag, t, &ii, &ww, true);
+    const bool ok = P.E <= 4 * kWave ? topk_token<4>(P, tag, t, hs, &ii, &ww, true)
+                                     : topk_token<kMaxE / kWave>(P, tag, t, hs, &ii, &ww, true);
     if (!ok) return false;
     if (lane < P.k) {
       const uint32_t wb = __builtin_bit_cast(uint32_t, ww);
@@ -2871,7 +2934,8 @@ static Layout make_layout(const moe_mxfp4_dims* dm, int32_t k) {
   const size_t T = (size_t)dm->T, E = (size_t)dm->E, TK = T * (size_t)k;
   size_t o = 0;
   L.hdr = o; o = align_up(o + kHdrBytes);
-  L.lgp = o; o = align_up(o + T * ((E + 1) & ~(size_t)1) * 8);
+  // two arrays of partial logits where the MFMA router splits K (router_halves)
+  L.lgp = o; o = align_up(o + (T > (size_t)kRouterMfmaT ? 2 : 1) * T * ((E + 1) & ~(size_t)1) * 8);
   L.tk = o; o = align_up(o + (size_t)kTopkRep * TK * 16);
   L.hq = o; o = align_up(o + TK * (size_t)dm->ffn * 8);
   L.yq = o; o = align_up(o + TK * (size_t)dm->d * 8);
