@@ -148,6 +148,38 @@ def stream_read_ref(dev, stream, gib: int = 4, reps: int = 10) -> dict:
     return {"GBs": round(best[0], 1), "how": f"{best[1]} over a {gib} GiB buffer, mean of {reps} (the faster of two)"}
 
 
+# Trace stamps of the persistent launch (MOE_OPT_TRACE): slot -> end of phase.
+TRACE_PHASES = [("router", 1), ("topk_published", 7), ("topk_read", 2), ("permutation_and_split", 3),
+                ("gate_up", 4), ("first_h", 8), ("down", 5), ("combine", 6)]
+
+
+def trace_phases(moe, torch, np, dims, cfg, xt, wrt, reps_p, reps_s, out, ws, calls):
+    """Untimed calls with the trace option; per phase the median over calls of
+    the median and the maximum over workgroups of the phase's end, in us from
+    the call's first workgroup start (wall clock, 100 MHz)."""
+    G = moe.persistent_grid(dims, cfg.k)
+    opts = moe.Options(moe.MOE_OPT_TRACE, 0, 0)
+    rows, plain = [], []
+    for j in range(calls):
+        moe.forward(xt, wrt, reps_p[j % len(reps_p)], reps_s[j % len(reps_s)], cfg.k, out=out, workspace=ws,
+                    dims=dims, options=opts)
+        torch.cuda.synchronize()
+        rows.append(moe.intermediates(ws, dims, cfg.k)["trace"][:G].cpu().numpy().astype(np.int64))
+    if moe.status(ws) != moe.MOE_OK:
+        raise RuntimeError("device watchdog fired during the traced calls")
+    tr = np.stack(rows)  # [calls, G, slots]
+    rel = (tr - tr[:, :, 0].min(axis=1)[:, None, None]) / 100.0
+    res = {"calls": calls, "grid": G, "unit": "us from the first workgroup's start",
+           "stat": "median over calls of (median over workgroups, max over workgroups)"}
+    for name, slot in TRACE_PHASES:
+        v = rel[:, :, slot]
+        if (v < 0).any() or (v > 1e6).any():  # a stamp this variant does not write
+            res[name] = None
+            continue
+        res[name] = [round(float(np.median(np.median(v, axis=1))), 1), round(float(np.median(v.max(axis=1))), 1)]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +197,9 @@ def main():
     ap.add_argument("--staged", action="store_true", help="time the one-launch-per-step path instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--phases", type=int, default=0, metavar="CALLS",
+                    help="after the timed steps, this many untimed calls with the trace option: per-phase "
+                         "wall-clock stamps of every workgroup, reported as \"phases\" in the line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -259,6 +294,10 @@ def main():
         raise RuntimeError("device watchdog fired during the timed steps")
     launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
+    phases = None
+    if args.phases > 0 and not args.staged:
+        phases = trace_phases(moe, torch, np, dims, cfg, xt, wrt, reps_p, reps_s, out, ws, args.phases)
+
     ref = stream_read_ref(dev, stream)
 
     it = moe.intermediates(ws, dims, cfg.k)
@@ -325,6 +364,8 @@ def main():
         "host": host_info(),
         "stream_read_ref": dict(ref, layer_kernel_frac=round(kern_gbs / ref["GBs"], 4)),
     }
+    if phases is not None:
+        result["phases"] = phases
 
     if not args.no_cpu_baseline:
         from oracle import oracle
