@@ -86,6 +86,7 @@ SMALL = [
     dict(T=100, d=800, F=96, E=3, k=2),        # MFMA path: partial K blocks and partial row units
     dict(T=96, d=800, F=256, E=4, k=2),        # MFMA path: gate/up scales byte by byte, down scales 8 bytes a row
     dict(T=824, d=256, F=128, E=160, k=2),     # MFMA router with 32-token units (520 tiles), the last 24 tokens past T
+    dict(T=128, d=256, F=128, E=1024, k=8),    # MFMA path at E = 1024: hundreds of active experts of ~1 token each
 ]
 
 
