@@ -356,25 +356,27 @@ def test_small_grid_option(env):
 
 
 def test_mfma_grid_options(env):
-    """MFMA path on grids of 1, 3, 37, 40, 64 and 100 workgroups: one chunk
+    """MFMA path (both router splits) on grids of 1, 3, 37, 40, 64 and 100 workgroups: one chunk
     for the whole grid (37, 100: not a multiple of 8), 5 and 8 workgroups per
     XCD chunk (40, 64), more than 64 per chunk (100: down units dealt by index
     instead of by gate/up work).  Every grid covers every unit once: the
     output matches the oracle and, as a unit computes the same values on
     whichever workgroup runs it, equals the default grid's bit for bit."""
     torch, moe, oracle, synth = env
-    cfg = synth.Config("mfma_grid", T=100, d=2048, F=2080, E=16, k=4)
-    x, wr, p, s = inputs_for(synth, cfg)
-    ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
-    xt, wrt, pt, st = to_device(torch, x, wr, p, s)
-    base = moe.forward(xt, wrt, pt, st, cfg.k).cpu().numpy()
-    assert rel_err(base, ref.out) <= OUT_TOL
-    for g in (1, 3, 37, 40, 64, 100):
-        print(f"[case] mfma grid {g}", flush=True)
-        out = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(0, 0, g))
-        torch.cuda.synchronize()
-        got = out.cpu().numpy()
-        assert np.array_equal(got.view(np.uint32), base.view(np.uint32)), g
+    # the router splits K in two (16 tiles), then takes 32-token units (520 tiles)
+    for shape in (dict(T=100, d=2048, F=2080, E=16, k=4), dict(T=824, d=256, F=128, E=160, k=2)):
+        cfg = synth.Config("mfma_grid", **shape)
+        x, wr, p, s = inputs_for(synth, cfg)
+        ref = oracle.forward(x, wr, p, s, cfg.k, cfg.F)
+        xt, wrt, pt, st = to_device(torch, x, wr, p, s)
+        base = moe.forward(xt, wrt, pt, st, cfg.k).cpu().numpy()
+        assert rel_err(base, ref.out) <= OUT_TOL
+        for g in (1, 3, 37, 40, 64, 100):
+            print(f"[case] mfma T={cfg.T} grid {g}", flush=True)
+            out = moe.forward(xt, wrt, pt, st, cfg.k, options=moe.Options(0, 0, g))
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), base.view(np.uint32)), (cfg.T, g)
 
 
 def test_cooperative_launch_option(env):
